@@ -1,0 +1,153 @@
+"""CPU oracle for QSA block selection -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP library and its Python binding
+never import it, and it imports nothing from them: the two sides share no code.
+
+The arithmetic lives in ``qsa_oracle.c`` (plain C, gcc -O2, no fast-math) and
+is reached through ``ctypes``; this module only marshals numpy arrays.
+
+What it computes (pages: "#3108 perf(hip): optimize exact QSA block scoring and
+top-k selection on gfx12", Summary items 1-2; "#337 hip: gfx12 (RDNA4) QSA
+select - WMMA block scorer, prompt-aware top-k dispatch", What items 1-2):
+
+* ``scores_f64(q, kblk, active_blocks)``: FP64 block scores
+  ``s[i][b] = sum_h sum_d q[i][h][d] * kblk[b][h][d]`` for ``b < active_blocks``.
+* ``topk(scores, k)``: for each row, the ids of the k largest scores, ties to
+  the lower id, in rank order; slots past the row length hold -1.
+* ``topk_f64(scores64, k)``: the same order on FP64 scores (diagnostic only).
+
+Every function here is pinned by tests/test_oracle.py (hand example, exact
+integer inputs, exact rationals, numpy float64 matmul, brute-force rank,
+numpy lexsort, invariants).  No function here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qsa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libqsa_oracle.so")
+
+OK, ERR_ARG, ERR_NAN, ERR_NOMEM = 0, 1, 2, 3
+_ERR_TEXT = {ERR_ARG: "bad argument", ERR_NAN: "NaN score in the active range",
+             ERR_NOMEM: "out of memory"}
+
+_lib = None
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+             "-ffp-contract=off", "-Wall", "-Wextra"]
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile one oracle C source into a shared library with plain gcc."""
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", *GCC_FLAGS, "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile qsa_oracle.c into oracle/libqsa_oracle.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        compile_source(_SRC, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.oracle_block_scores_f64.argtypes = [vp, vp, i64, i64, i64, i64, vp]
+    lib.oracle_block_scores_f64.restype = ctypes.c_int
+    lib.oracle_block_topk.argtypes = [vp, i64, i64, i64, vp]
+    lib.oracle_block_topk.restype = ctypes.c_int
+    lib.oracle_block_topk_f64.argtypes = [vp, i64, i64, i64, vp]
+    lib.oracle_block_topk_f64.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        _lib = _bind(_LIB_PATH)
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != OK:
+        raise OracleError(f"oracle status {rc}: {_ERR_TEXT.get(rc, 'unknown')}")
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data if a.size else None
+
+
+class Oracle:
+    """The oracle's three functions bound to one compiled copy of qsa_oracle.c.
+
+    The default copy is ``oracle.default()``; tests also bind deliberately
+    broken copies (mutants) to show that the pins catch plausible mistakes.
+    """
+
+    def __init__(self, lib):
+        self.lib = lib
+
+    def scores_f64(self, q: np.ndarray, kblk: np.ndarray, active_blocks: int) -> np.ndarray:
+        """FP64 scores of q[nq][heads][dim] against kblk[>=active_blocks][heads][dim]."""
+        q = np.ascontiguousarray(q, dtype=np.float32)
+        kblk = np.ascontiguousarray(kblk, dtype=np.float32)
+        nq, heads, dim = q.shape
+        if kblk.ndim != 3 or kblk.shape[1:] != (heads, dim) or kblk.shape[0] < active_blocks:
+            raise ValueError("kblk must be [>=active_blocks][heads][dim]")
+        out = np.empty((nq, active_blocks), dtype=np.float64)
+        _check(self.lib.oracle_block_scores_f64(_ptr(q), _ptr(kblk), nq, heads, dim,
+                                                active_blocks, _ptr(out)))
+        return out
+
+    def topk(self, scores: np.ndarray, k: int) -> np.ndarray:
+        """Rank-ordered top-k ids (int32, -1 padded) of each row of fp32 scores."""
+        scores = np.ascontiguousarray(scores, dtype=np.float32)
+        nq, a = scores.shape
+        ids = np.empty((nq, k), dtype=np.int32)
+        _check(self.lib.oracle_block_topk(_ptr(scores), nq, a, k, _ptr(ids)))
+        return ids
+
+    def topk_f64(self, scores: np.ndarray, k: int) -> np.ndarray:
+        """The same selection on FP64 scores (a diagnostic, never a gate)."""
+        scores = np.ascontiguousarray(scores, dtype=np.float64)
+        nq, a = scores.shape
+        ids = np.empty((nq, k), dtype=np.int32)
+        _check(self.lib.oracle_block_topk_f64(_ptr(scores), nq, a, k, _ptr(ids)))
+        return ids
+
+
+def default() -> Oracle:
+    return Oracle(_load())
+
+
+def load_from(path: str) -> Oracle:
+    """Bind a separately compiled copy of the oracle (used for mutant checks)."""
+    return Oracle(_bind(path))
+
+
+def scores_f64(q, kblk, active_blocks):
+    return default().scores_f64(q, kblk, active_blocks)
+
+
+def topk(scores, k):
+    return default().topk(scores, k)
+
+
+def topk_f64(scores, k):
+    return default().topk_f64(scores, k)

@@ -1,0 +1,163 @@
+/*
+ * CPU oracle for QSA block selection (exact block scoring + per-query top-k).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously correct
+ * definition that the GPU path is checked against.  Only the test suite, the
+ * smoke check and the benchmark's CPU-baseline leg may load it.  It shares no
+ * code, header, table or constant with the HIP library, and the HIP library
+ * never calls it.
+ *
+ * Built with plain gcc (-O2, no -ffast-math, no FTZ); see oracle/__init__.py.
+ *
+ * Sources (web pages on the selection path of a closed inference engine):
+ *   [P1] "#3108 perf(hip): optimize exact QSA block scoring and top-k selection
+ *        on gfx12", Summary item 1 (a block score is the sum over the query's
+ *        heads of per-head dot products against the block's key summary) and
+ *        item 2 (radix top-k selection of blocks per query).
+ *   [P4] "#337 hip: gfx12 (RDNA4) QSA select - WMMA block scorer, prompt-aware
+ *        top-k dispatch", What item 1 (top-k runs over the active blocks, not
+ *        the capacity) and item 2 (scores are checked against an FP64
+ *        reference; top-k ids must equal the reference selection on the same
+ *        scores).
+ *
+ * Readings where the pages are silent (listed in the design notes too):
+ *   - layouts are dense row-major: q[nq][heads][dim], kblk[blocks][heads][dim],
+ *     scores[nq][active_blocks], ids[nq][k];
+ *   - heads are combined by a sum, with no 1/sqrt(d) or other scale;
+ *   - ties in score go to the lower block id; -0.0 and +0.0 are equal;
+ *   - ids come out in rank order (score descending, id ascending), and slots
+ *     past active_blocks (k > active_blocks) hold -1;
+ *   - scores must be finite (NaN is reported as an error).
+ *
+ * Pins (what this oracle is checked against, not itself): a hand-worked
+ * 3-block example, exact integer inputs vs numpy int64 matmul, exact rationals
+ * (fractions.Fraction) on tiny inputs, numpy float64 matmul, brute-force rank
+ * on tiny rows with heavy ties, numpy lexsort, and invariants; see
+ * tests/test_oracle.py.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+/* Status codes of this oracle (independent of the HIP library's codes). */
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG 1
+#define ORACLE_ERR_NAN 2
+#define ORACLE_ERR_NOMEM 3
+
+/*
+ * Block scores in FP64 ([P1] Summary item 1; [P4] What item 2):
+ *   out[i][b] = sum_{h<heads} sum_{d<dim} q[i][h][d] * kblk[b][h][d]
+ * for 0 <= i < nq and 0 <= b < active_blocks.
+ *
+ * Every product of two fp32 numbers is exact in FP64 (24+24 <= 53 significand
+ * bits), so the only rounding is in the heads*dim-1 sequential additions.
+ * Rows b >= active_blocks of kblk are never read.
+ */
+int oracle_block_scores_f64(const float *q, const float *kblk, int64_t nq,
+                            int64_t heads, int64_t dim, int64_t active_blocks,
+                            double *out) {
+  if (nq < 0 || heads < 0 || dim < 0 || active_blocks < 0) return ORACLE_ERR_ARG;
+  if (nq == 0 || active_blocks == 0) return ORACLE_OK;
+  if (!q || !kblk || !out) return ORACLE_ERR_ARG;
+  for (int64_t i = 0; i < nq; ++i) {
+    for (int64_t b = 0; b < active_blocks; ++b) {
+      double s = 0.0;
+      for (int64_t h = 0; h < heads; ++h) {
+        for (int64_t d = 0; d < dim; ++d) {
+          const double qv = (double)q[(i * heads + h) * dim + d];
+          const double kv = (double)kblk[(b * heads + h) * dim + d];
+          s += qv * kv;
+        }
+      }
+      out[i * active_blocks + b] = s;
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* One candidate of a row: its score and its block id. */
+typedef struct {
+  double score;
+  int64_t id;
+} cand_t;
+
+/*
+ * The selection order: a comes before b when its score is larger, or the
+ * scores are equal and its id is smaller.  IEEE comparison, so -0.0 == +0.0.
+ * This is a strict total order on a row of finite scores, so the sorted row,
+ * and hence the top-k, is unique.
+ */
+static int cand_cmp(const void *pa, const void *pb) {
+  const cand_t *a = (const cand_t *)pa;
+  const cand_t *b = (const cand_t *)pb;
+  if (a->score > b->score) return -1;
+  if (a->score < b->score) return 1;
+  if (a->id < b->id) return -1;
+  if (a->id > b->id) return 1;
+  return 0;
+}
+
+/* Sort-based top-k of one row whose scores have already been widened. */
+static void topk_row(cand_t *c, int64_t active_blocks, int64_t k, int32_t *ids) {
+  qsort(c, (size_t)active_blocks, sizeof(cand_t), cand_cmp);
+  for (int64_t r = 0; r < k; ++r) ids[r] = (r < active_blocks) ? (int32_t)c[r].id : -1;
+}
+
+/*
+ * Top-k of fp32 scores ([P1] Summary item 2; [P4] What item 1, "top-k ids
+ * equal the reference's" on the same scores): for every row i, sort the block
+ * ids b in [0, active_blocks) by (score descending, id ascending) and write
+ * the first k of them to ids[i][0..k); slots r >= active_blocks get -1.
+ * A NaN score anywhere in the active range returns ORACLE_ERR_NAN.
+ */
+int oracle_block_topk(const float *scores, int64_t nq, int64_t active_blocks,
+                      int64_t k, int32_t *ids) {
+  if (nq < 0 || active_blocks < 0 || k < 0) return ORACLE_ERR_ARG;
+  if (nq == 0 || k == 0) return ORACLE_OK;
+  if (!ids || (active_blocks > 0 && !scores)) return ORACLE_ERR_ARG;
+  cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)(active_blocks > 0 ? active_blocks : 1));
+  if (!c) return ORACLE_ERR_NOMEM;
+  for (int64_t i = 0; i < nq; ++i) {
+    for (int64_t b = 0; b < active_blocks; ++b) {
+      const float s = scores[i * active_blocks + b];
+      if (isnan(s)) {
+        free(c);
+        return ORACLE_ERR_NAN;
+      }
+      c[b].score = (double)s; /* widening is exact and keeps the order */
+      c[b].id = b;
+    }
+    topk_row(c, active_blocks, k, ids + i * k);
+  }
+  free(c);
+  return ORACLE_OK;
+}
+
+/*
+ * The same top-k on FP64 scores.  Used only as a diagnostic (how often a
+ * selection on the rounded fp32 scores equals the selection on the FP64
+ * ones), never as a gate.
+ */
+int oracle_block_topk_f64(const double *scores, int64_t nq, int64_t active_blocks,
+                          int64_t k, int32_t *ids) {
+  if (nq < 0 || active_blocks < 0 || k < 0) return ORACLE_ERR_ARG;
+  if (nq == 0 || k == 0) return ORACLE_OK;
+  if (!ids || (active_blocks > 0 && !scores)) return ORACLE_ERR_ARG;
+  cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)(active_blocks > 0 ? active_blocks : 1));
+  if (!c) return ORACLE_ERR_NOMEM;
+  for (int64_t i = 0; i < nq; ++i) {
+    for (int64_t b = 0; b < active_blocks; ++b) {
+      const double s = scores[i * active_blocks + b];
+      if (isnan(s)) {
+        free(c);
+        return ORACLE_ERR_NAN;
+      }
+      c[b].score = s;
+      c[b].id = b;
+    }
+    topk_row(c, active_blocks, k, ids + i * k);
+  }
+  free(c);
+  return ORACLE_OK;
+}

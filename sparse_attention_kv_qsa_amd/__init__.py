@@ -1,0 +1,20 @@
+"""QSA block selection on MI355X (gfx950): exact block scoring + radix top-k.
+
+The compute lives in ``libqsa.so`` (hand-written HIP for CDNA4, C ABI declared
+in ``include/qsa.h``).  ``qsa_block_scores`` / ``qsa_block_topk`` here are thin
+ctypes bindings with the same names as the C entry points: they marshal torch
+tensors and the current HIP stream, nothing more.  There is no CPU fallback:
+calling them without the built library, or with tensors that are not on the
+GPU, raises.
+"""
+from .synth import WORKLOADS, HEADLINE, Workload, make_batch, make_random, fingerprint  # noqa: F401
+
+
+def __getattr__(name):
+    # The binding loads libqsa.so (and torch) on first use only, so the
+    # generator can be imported on hosts without the library.
+    if name in ("qsa_block_scores", "qsa_block_topk", "qsa_strerror", "QSAError",
+                "load_library", "library_path", "TOPK_MAX_K", "block_scores", "block_topk"):
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

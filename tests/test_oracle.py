@@ -1,0 +1,307 @@
+"""Pins of the CPU oracle against things other than itself (no GPU needed).
+
+The pages print no worked example, score values or id lists, so the oracle is
+pinned by: a hand-worked example (tests/golden/hand_3block.txt), exact integer
+inputs vs numpy int64 matmul, exact rationals, numpy float64 matmul, the
+brute-force rank definition, numpy lexsort, closed-form special rows and
+invariants.  ``test_mutants_are_caught`` plants plausible mistakes in copies of
+the oracle's C source and shows that every one fails some pin.
+"""
+from __future__ import annotations
+
+import os
+import random
+import re
+import tempfile
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from checks import brute_force_topk, score_gate, topk_invariants
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_3block.txt")
+ORC = oracle.default()
+
+
+def load_hand_example():
+    heads = dim = None
+    q, b, scores, topks = [], [], {}, []
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, rest = line.split(None, 1)
+            if key == "heads":
+                heads = int(rest)
+            elif key == "dim":
+                dim = int(rest)
+            elif key == "q":
+                q.append([float(x) for x in rest.split()])
+            elif key == "b":
+                b.append([float(x) for x in rest.split()])
+            elif key == "scores":
+                i, vals = rest.split(":")
+                scores[int(i)] = [float(x) for x in vals.split()]
+            elif key == "topk":
+                head, vals = rest.split(":")
+                i, k = (int(x) for x in head.split())
+                topks.append((i, k, [int(x) for x in vals.split()]))
+    q = np.array(q, np.float32).reshape(-1, heads, dim)
+    b = np.array(b, np.float32).reshape(-1, heads, dim)
+    return q, b, scores, topks
+
+
+# ----------------------------------------------------------------- pins ----
+
+def pin_hand_example(orc):
+    q, b, scores, topks = load_hand_example()
+    s = orc.scores_f64(q, b, b.shape[0])
+    for i, want in scores.items():
+        if list(s[i]) != want:
+            return f"hand scores row {i}: {list(s[i])} != {want}"
+    s32 = s.astype(np.float32)
+    for i, k, want in topks:
+        got = orc.topk(s32[i:i + 1], k)[0].tolist()
+        if got != want:
+            return f"hand top-k q{i} k={k}: {got} != {want}"
+    return None
+
+
+INT_SHAPES = [(1, 1, 1, 1), (2, 3, 5, 7), (5, 2, 7, 3), (3, 4, 64, 33), (7, 1, 12, 19), (4, 4, 128, 9)]
+
+
+def pin_integer_exact(orc):
+    """Small-integer inputs: every fp64 partial sum is an exact integer, so the
+    oracle must equal numpy's int64 matmul exactly (an independent routine)."""
+    rng = np.random.default_rng(1)
+    for nq, heads, dim, a in INT_SHAPES:
+        q = rng.integers(-8, 9, (nq, heads, dim))
+        kb = rng.integers(-8, 9, (a + 2, heads, dim))
+        want = q.reshape(nq, -1).astype(np.int64) @ kb[:a].reshape(a, -1).astype(np.int64).T
+        got = orc.scores_f64(q.astype(np.float32), kb.astype(np.float32), a)
+        if not np.array_equal(got, want.astype(np.float64)):
+            return f"integer shape {(nq, heads, dim, a)}: mismatch"
+    return None
+
+
+def pin_float64_matmul(orc):
+    rng = np.random.default_rng(2)
+    for nq, heads, dim, a in [(3, 4, 64, 50), (2, 3, 5, 17), (6, 1, 300, 11)]:
+        q = rng.standard_normal((nq, heads, dim)).astype(np.float32)
+        kb = rng.standard_normal((a, heads, dim)).astype(np.float32)
+        want = q.reshape(nq, -1).astype(np.float64) @ kb.reshape(a, -1).astype(np.float64).T
+        got = orc.scores_f64(q, kb, a)
+        scale = np.abs(want).max()
+        if np.abs(got - want).max() > 1e-12 * scale:
+            return f"float64 matmul shape {(nq, heads, dim, a)}: mismatch"
+    return None
+
+
+def pin_exact_rationals(orc):
+    """Exact value by fractions.Fraction; the FP64 sum may differ only by the
+    rounding of its K-1 additions: |s64 - exact| <= (K-1) * 2^-53 * sum|products|."""
+    rng = np.random.default_rng(3)
+    nq, heads, dim, a = 2, 2, 3, 4
+    q = rng.standard_normal((nq, heads, dim)).astype(np.float32)
+    kb = rng.standard_normal((a, heads, dim)).astype(np.float32)
+    got = orc.scores_f64(q, kb, a)
+    K = heads * dim
+    for i in range(nq):
+        for b in range(a):
+            prods = [Fraction(float(x)) * Fraction(float(y))
+                     for x, y in zip(q[i].ravel(), kb[b].ravel())]
+            exact = sum(prods, Fraction(0))
+            bound = (K - 1) * 2.0 ** -53 * float(sum(abs(p) for p in prods))
+            if abs(Fraction(got[i, b]) - exact) > Fraction(bound):
+                return f"rational ({i},{b}) outside the rounding bound"
+    return None
+
+
+TIE_VALUES = [-1.0, -0.0, 0.0, 1.0, 2.0]
+
+
+def pin_topk_brute_force(orc):
+    rnd = random.Random(4)
+    for a in range(0, 13):
+        for _ in range(6):
+            row = [rnd.choice(TIE_VALUES) for _ in range(a)]
+            for k in range(0, a + 3):
+                got = orc.topk(np.array([row], np.float32).reshape(1, a), k)[0].tolist()
+                if got != brute_force_topk(row, k):
+                    return f"brute force row={row} k={k}: {got}"
+    return None
+
+
+def pin_topk_lexsort(orc):
+    rng = np.random.default_rng(5)
+    for a, k in [(100, 10), (1000, 64), (4097, 512), (300, 300), (50, 80)]:
+        s = np.round(rng.standard_normal((4, a)) * 4).astype(np.float32)  # many ties
+        got = orc.topk(s, k)
+        for i in range(4):
+            order = np.lexsort((np.arange(a), -s[i].astype(np.float64)))[: min(k, a)]
+            want = np.full(k, -1, np.int64)
+            want[: len(order)] = order
+            if not np.array_equal(got[i], want):
+                return f"lexsort a={a} k={k} row {i}"
+    return None
+
+
+def pin_topk_special_rows(orc):
+    a, k = 37, 9
+    const = np.full((1, a), 3.5, np.float32)
+    dec = np.arange(a, 0, -1, dtype=np.float32)[None]
+    inc = np.arange(a, dtype=np.float32)[None]
+    checks = [
+        (const, list(range(k))),
+        (dec, list(range(k))),
+        (inc, list(range(a - 1, a - 1 - k, -1))),
+    ]
+    for s, want in checks:
+        if orc.topk(s, k)[0].tolist() != want:
+            return "special row"
+    full = orc.topk(inc, a)[0].tolist()
+    if full != list(range(a - 1, -1, -1)):
+        return "k = A is not the full sorted permutation"
+    if orc.topk(np.zeros((2, 0), np.float32), 3).tolist() != [[-1, -1, -1]] * 2:
+        return "A = 0 must give all -1"
+    return None
+
+
+def pin_topk_invariants(orc):
+    rng = np.random.default_rng(6)
+    for a, k in [(200, 17), (513, 64), (64, 64), (10, 30)]:
+        s = np.round(rng.standard_normal((3, a)) * 3).astype(np.float32)
+        bad = topk_invariants(s, orc.topk(s, k), k)
+        if bad:
+            return f"invariants a={a} k={k}: {bad[:2]}"
+    return None
+
+
+def pin_active_rows_only(orc):
+    """Rows past active_blocks are never read: NaN there changes nothing."""
+    q, kb = np.ones((2, 2, 3), np.float32), np.ones((6, 2, 3), np.float32)
+    kb[4:] = np.nan
+    s = orc.scores_f64(q, kb, 4)
+    if not np.all(s == 6.0):
+        return "poison rows were read"
+    return None
+
+
+PINS = [pin_hand_example, pin_integer_exact, pin_float64_matmul, pin_exact_rationals,
+        pin_topk_brute_force, pin_topk_lexsort, pin_topk_special_rows,
+        pin_topk_invariants, pin_active_rows_only]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_oracle_pins(pin):
+    assert pin(ORC) is None
+
+
+# -------------------------------------------------- further properties ----
+
+def test_power_of_two_scaling_is_exact():
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((3, 4, 16)).astype(np.float32)
+    kb = rng.standard_normal((20, 4, 16)).astype(np.float32)
+    s = ORC.scores_f64(q, kb, 20)
+    assert np.array_equal(ORC.scores_f64(q * 4, kb, 20), s * 4)
+    assert np.array_equal(ORC.scores_f64(q, kb * 0.5, 20), s * 0.5)
+
+
+def test_block_permutation_permutes_scores_bitwise():
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((3, 4, 16)).astype(np.float32)
+    kb = rng.standard_normal((30, 4, 16)).astype(np.float32)
+    perm = rng.permutation(30)
+    assert np.array_equal(ORC.scores_f64(q, kb[perm], 30), ORC.scores_f64(q, kb, 30)[:, perm])
+
+
+def test_nan_score_is_reported():
+    s = np.zeros((1, 5), np.float32)
+    s[0, 3] = np.nan
+    with pytest.raises(oracle.OracleError):
+        ORC.topk(s, 2)
+
+
+def test_infinities_order_naturally():
+    s = np.array([[1.0, np.inf, -np.inf, 0.0]], np.float32)
+    assert ORC.topk(s, 4)[0].tolist() == [1, 0, 3, 2]
+
+
+def test_f64_selection_matches_fp32_on_exact_values():
+    rng = np.random.default_rng(9)
+    s = np.round(rng.standard_normal((4, 300)) * 8)
+    assert np.array_equal(ORC.topk_f64(s, 40), ORC.topk(s.astype(np.float32), 40))
+
+
+# ------------------------------------------------ negative controls ----
+
+def test_checkers_catch_planted_result_errors():
+    rng = np.random.default_rng(10)
+    s = np.round(rng.standard_normal((1, 400)) * 3).astype(np.float32)
+    k = 50
+    ids = ORC.topk(s, k)
+    assert topk_invariants(s, ids, k) == []
+    # swap two tied ids inside the selection
+    row = ids[0].copy()
+    v = s[0, row]
+    r = next(r for r in range(k - 1) if v[r] == v[r + 1])
+    bad = ids.copy()
+    bad[0, r], bad[0, r + 1] = row[r + 1], row[r]
+    assert topk_invariants(s, bad, k)
+    # nudge the last selected score one ulp below the best unselected one
+    s2 = s.copy()
+    last = ids[0, -1]
+    mask = np.ones(400, bool)
+    mask[ids[0]] = False
+    best_unsel = s[0, mask].max()
+    s2[0, last] = np.nextafter(best_unsel, np.float32(-np.inf))
+    assert topk_invariants(s2, ids, k) or not np.array_equal(ORC.topk(s2, k), ids)
+
+
+def test_score_gate_catches_a_shift():
+    rng = np.random.default_rng(11)
+    s64 = rng.standard_normal((4, 100)) * 20
+    ok, _ = score_gate(s64.astype(np.float32), s64)
+    assert ok
+    bad = s64.astype(np.float32).astype(np.float64)
+    bad[2, 7] += 2e-6 * np.abs(s64).max()
+    assert not score_gate(bad, s64)[0]
+
+
+# Each mutant is a plausible mistake in the oracle's C source: (pattern, replacement).
+MUTANTS = {
+    "dropped last head": (r"h < heads; \+\+h", "h < heads - 1; ++h"),
+    "dropped first dim term": (r"int64_t d = 0; d < dim", "int64_t d = 1; d < dim"),
+    "wrong sign": (r"s \+= qv \* kv;", "s -= qv * kv;"),
+    "q squared": (r"s \+= qv \* kv;", "s += qv * qv;"),
+    "kblk transposed": (r"kblk\[\(b \* heads \+ h\) \* dim \+ d\]", "kblk[(b * dim + d) * heads + h]"),
+    "q index drops the head": (r"q\[\(i \* heads \+ h\) \* dim \+ d\]", "q[i * heads * dim + d]"),
+    "output transposed": (r"out\[i \* active_blocks \+ b\]", "out[b * nq + i]"),
+    "ties to the higher id": (r"if \(a->id < b->id\) return -1;\n  if \(a->id > b->id\) return 1;",
+                              "if (a->id > b->id) return -1;\n  if (a->id < b->id) return 1;"),
+    "ascending order": (r"if \(a->score > b->score\) return -1;\n  if \(a->score < b->score\) return 1;",
+                        "if (a->score < b->score) return -1;\n  if (a->score > b->score) return 1;"),
+    "pad with zero": (r": -1;", ": 0;"),
+    "signed-zero unequal": (r"c\[b\]\.score = \(double\)s;", "c[b].score = signbit(s) ? -1e-300 : (double)s;"),
+    "score via float accumulation": (r"double s = 0\.0;", "float s = 0.0f;"),
+}
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_mutants_are_caught(name):
+    pattern, repl = MUTANTS[name]
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "qsa_oracle.c")).read()
+    mutated, n = re.subn(pattern, repl, src)
+    assert n >= 1, f"mutation {name!r} did not apply"
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "mutant.c")
+        with open(path, "w") as f:
+            f.write(mutated)
+        lib = oracle.compile_source(path, os.path.join(d, "libmutant.so"))
+        mutant = oracle.load_from(lib)
+        failures = [p.__name__ for p in PINS if p(mutant) is not None]
+    assert failures, f"no pin catches the mutant {name!r}"

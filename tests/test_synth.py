@@ -1,0 +1,62 @@
+"""The seeded input generator: determinism and workload structure (no GPU)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from sparse_attention_kv_qsa_amd import synth
+
+
+def test_workload_table():
+    w = synth.WORKLOADS
+    assert [x.name for x in w.values()] == ["tiny-decode", "prompt-32k", "decode-128k",
+                                            "prompt-128k", "prompt-256k-tie"]
+    assert (w["tiny-decode"].active, w["tiny-decode"].K, w["tiny-decode"].k) == (512, 256, 64)
+    assert (w["prompt-32k"].nq, w["prompt-32k"].active, w["prompt-32k"].k) == (256, 8193, 256)
+    assert (w["decode-128k"].active, w["decode-128k"].capacity) == (32770, 65538)
+    assert (w["prompt-128k"].n_needles, w["prompt-32k"].n_needles) == (328, 82)
+    assert w["prompt-256k-tie"].n_needles == 66
+    # a 262,144-cell capacity is max-context/4 + 2 blocks
+    assert w["prompt-128k"].capacity == 262144 // 4 + 2
+
+
+def test_deterministic_in_seed():
+    w = synth.WORKLOADS["tiny-decode"]
+    a, b = synth.make_batch(w), synth.make_batch(w)
+    assert synth.fingerprint(a.q) == synth.fingerprint(b.q)
+    assert synth.fingerprint(a.kblk) == synth.fingerprint(b.kblk)
+    c = synth.make_batch(w, seed=1)
+    assert synth.fingerprint(a.q) != synth.fingerprint(c.q)
+
+
+def test_needles_and_poison():
+    w = synth.Workload("t", nq=8, heads=2, dim=16, active=500, capacity=520, k=10,
+                       needle_frac=0.02, poison=True)
+    bt = synth.make_batch(w)
+    assert len(bt.needle_blocks) == 10 and len(set(bt.needle_blocks.tolist())) == 10
+    assert np.all(np.isnan(bt.kblk[500:])) and np.all(np.isfinite(bt.kblk[:500]))
+    for b, j in zip(bt.needle_blocks, bt.needle_queries):
+        # a needle is 0.8*q_j + 0.2*noise: strongly aligned with q_j
+        x, y = bt.kblk[b].ravel(), bt.q[j].ravel()
+        assert np.dot(x, y) / (np.linalg.norm(x) * np.linalg.norm(y)) > 0.9
+
+
+def test_tie_workload_has_few_distinct_rows():
+    w = synth.Workload("t", nq=4, heads=2, dim=8, active=3000, capacity=3000, k=100,
+                       needle_frac=0.001, tie_vectors=64)
+    bt = synth.make_batch(w)
+    distinct = np.unique(bt.kblk.reshape(w.active, -1), axis=0)
+    assert len(distinct) <= 64 + w.n_needles
+
+
+def test_integer_inputs_range():
+    q, kb = synth.make_random(3, 4, 8, 20, capacity=24, integer=True)
+    assert q.dtype == np.float32 and np.all(np.abs(q) <= 8) and np.all(q == np.round(q))
+    assert np.all(np.isnan(kb[20:]))
+
+
+@pytest.mark.slow
+def test_full_workload_shapes():
+    bt = synth.make_batch(synth.WORKLOADS["prompt-32k"])
+    assert bt.q.shape == (256, 4, 128) and bt.kblk.shape == (8193, 4, 128)
+    assert bt.q.dtype == np.float32 and bt.kblk.dtype == np.float32
