@@ -1,0 +1,106 @@
+/*
+ * qsa.h -- C ABI of libqsa.so: QSA block selection on AMD Instinct MI355X
+ * (gfx950, CDNA4, wave64).
+ *
+ * QSA keeps the KV cache in blocks of 4 cells, each with a key summary of the
+ * same shape as a query ([heads][dim] fp32).  Selection has two steps:
+ *
+ *   1. block scoring: for every query i and every ACTIVE block b,
+ *        score[i][b] = sum_{h<heads} sum_{d<dim} q[i][h][d] * kblk[b][h][d]
+ *      i.e. per-head dot products summed over the heads (page "#3108
+ *      perf(hip): optimize exact QSA block scoring and top-k selection on
+ *      gfx12", Summary item 1: the per-head reductions that make up a 4-head
+ *      block score);
+ *   2. per-query top-k of the active blocks by score, ties to the lower block
+ *      id (same page, Summary item 2: radix top-k with 256-bin digits; page
+ *      "#337 hip: gfx12 (RDNA4) QSA select - WMMA block scorer, prompt-aware
+ *      top-k dispatch", What item 1: selection work follows the active block
+ *      count, never the capacity).
+ *
+ * Conventions for every entry point:
+ *   - Every data pointer is a DEVICE pointer on the current HIP device, owned
+ *     by the caller.  The library allocates nothing, keeps no global state and
+ *     may be called from several host threads at once.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL = the default stream).  The call returns once the work is
+ *     enqueued; results are valid after the stream is synchronised.
+ *   - Invalid arguments are rejected before anything is enqueued, and the
+ *     status is returned synchronously.  Faults inside kernels surface at the
+ *     caller's next synchronisation.
+ *   - Layouts are dense and row-major, without padding.  Sizes are ints;
+ *     index arithmetic inside is 64-bit.
+ *   - Results are deterministic: the same inputs give bitwise-identical
+ *     scores and ids on every call (no atomics take part in score arithmetic,
+ *     and the selection order is a strict total order).
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define QSA_OK 0
+#define QSA_ERR_NULL 1   /* a required pointer is NULL                              */
+#define QSA_ERR_SHAPE 2  /* a size < 0, or heads*dim not a multiple of 4 in [4, QSA_MAX_HEAD_DIM] */
+#define QSA_ERR_K 3      /* k < 0 or k > QSA_TOPK_MAX_K                             */
+#define QSA_ERR_ALIGN 4  /* q or kblk not 16-byte aligned, scores/ids not 4-byte aligned */
+#define QSA_ERR_LAUNCH 5 /* the HIP runtime rejected a launch (hipGetLastError)     */
+
+/* Largest heads*dim (elements of one query or one block summary). */
+#define QSA_MAX_HEAD_DIM 4096
+/* Largest k accepted by qsa_block_topk. */
+#define QSA_TOPK_MAX_K 4096
+
+/*
+ * qsa_block_scores -- exact block scores (step 1 above).
+ *
+ *   q       [nq][heads][dim] fp32, 16-byte aligned.
+ *   kblk    [>= active_blocks][heads][dim] fp32, 16-byte aligned.  Only rows
+ *           [0, active_blocks) are read; rows past them (the rest of the
+ *           capacity) are never touched and may hold anything.
+ *   scores  out: [nq][active_blocks] fp32, row stride active_blocks.
+ *
+ * Arithmetic is fp32 in a fixed order that does not depend on a block's
+ * position, so blocks with identical summaries get bitwise-identical scores
+ * within a call.  Small nq (<= 8) uses a bandwidth-bound per-block dot
+ * product; larger nq uses fp32 matrix-core (MFMA) tiles with one partial sum
+ * per quarter of heads*dim, combined as (p0 + p1) + (p2 + p3).  Either way the
+ * error against an exact (FP64) evaluation stays well inside
+ * 1e-6 * max|score| for N(0,1) inputs.
+ *
+ * nq == 0 or active_blocks == 0 is a successful no-op.  Non-finite inputs give
+ * non-finite scores.
+ */
+int qsa_block_scores(const float *q, const float *kblk, int nq, int heads, int dim,
+                     int active_blocks, float *scores, void *stream);
+
+/*
+ * qsa_block_topk -- per-query top-k of the active blocks (step 2 above).
+ *
+ *   scores  [nq][active_blocks] fp32 (row stride active_blocks), e.g. the
+ *           output of qsa_block_scores.  May be NULL when active_blocks == 0.
+ *   ids     out: [nq][k] int32.  Row i lists the k best block ids of query i
+ *           in rank order: score descending, equal scores by ascending id.
+ *           -0.0 and +0.0 are equal.  When k > active_blocks, slots
+ *           [active_blocks, k) hold -1 (so active_blocks == 0 gives all -1).
+ *
+ * The result is exact on the given scores: it equals a full sort of each row
+ * by (score desc, id asc) cut to k.  Scores must not be NaN (a NaN makes the
+ * row's result unspecified, though still a set of valid ids).  The kernel's
+ * work and dispatch depend on active_blocks only.
+ *
+ * nq == 0 or k == 0 is a successful no-op.
+ */
+int qsa_block_topk(const float *scores, int nq, int active_blocks, int k, int *ids,
+                   void *stream);
+
+/* Human-readable text of a status code (a static string; never NULL). */
+const char *qsa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

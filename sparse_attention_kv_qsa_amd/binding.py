@@ -1,0 +1,128 @@
+"""ctypes binding of libqsa.so (C ABI in include/qsa.h).
+
+Argument marshalling only: tensors are checked for dtype, device, layout and
+shape, outputs are allocated with torch when the caller passes none, and the
+work is enqueued on the tensor device's current torch stream.  Every step of
+the computation runs in the library's HIP kernels.  There is no fallback: a
+missing library, or tensors that are not on a GPU, raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libqsa.so"
+
+# Mirrors of include/qsa.h.
+QSA_OK, QSA_ERR_NULL, QSA_ERR_SHAPE, QSA_ERR_K, QSA_ERR_ALIGN, QSA_ERR_LAUNCH = 0, 1, 2, 3, 4, 5
+QSA_MAX_HEAD_DIM = 4096
+TOPK_MAX_K = 4096
+
+# Entry points declared in include/qsa.h: name -> (restype, argtypes).
+_VP, _I = ctypes.c_void_p, ctypes.c_int
+SIGNATURES = {
+    "qsa_block_scores": (_I, [_VP, _VP, _I, _I, _I, _I, _VP, _VP]),
+    "qsa_block_topk": (_I, [_VP, _I, _I, _I, _VP, _VP]),
+    "qsa_strerror": (ctypes.c_char_p, [_I]),
+}
+
+_lib = None
+
+
+class QSAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({qsa_strerror(status)})")
+
+
+def library_path() -> str:
+    return os.environ.get("QSA_LIBRARY", os.path.join(_HERE, _LIB_NAME))
+
+
+def load_library():
+    """Load libqsa.so once and attach the C signatures; raises if it is not built."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -m sparse_attention_kv_qsa_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def qsa_strerror(status: int) -> str:
+    return load_library().qsa_strerror(int(status)).decode()
+
+
+def _stream_handle(device: torch.device):
+    return torch.cuda.current_stream(device).cuda_stream or None
+
+
+def _require_gpu_f32(name: str, t: torch.Tensor, ndim: int):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32, got {t.dtype}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+
+
+def qsa_block_scores(q: torch.Tensor, kblk: torch.Tensor, active_blocks: int | None = None,
+                     scores: torch.Tensor | None = None) -> torch.Tensor:
+    """Scores [nq, active_blocks] of q [nq, heads, dim] against kblk [C, heads, dim].
+
+    Only rows [0, active_blocks) of kblk are read (default: all C rows).
+    """
+    _require_gpu_f32("q", q, 3)
+    _require_gpu_f32("kblk", kblk, 3)
+    nq, heads, dim = q.shape
+    if kblk.shape[1:] != q.shape[1:] or kblk.device != q.device:
+        raise ValueError("kblk must be [capacity, heads, dim] on q's device")
+    a = kblk.shape[0] if active_blocks is None else int(active_blocks)
+    if not 0 <= a <= kblk.shape[0]:
+        raise ValueError(f"active_blocks={a} outside [0, {kblk.shape[0]}]")
+    if scores is None:
+        scores = torch.empty((nq, a), dtype=torch.float32, device=q.device)
+    else:
+        _require_gpu_f32("scores", scores, 2)
+        if tuple(scores.shape) != (nq, a) or scores.device != q.device:
+            raise ValueError(f"scores must be [{nq}, {a}] on q's device")
+    with torch.cuda.device(q.device):
+        st = load_library().qsa_block_scores(q.data_ptr(), kblk.data_ptr(), nq, heads, dim, a,
+                                             scores.data_ptr(), _stream_handle(q.device))
+    if st != QSA_OK:
+        raise QSAError(st, "qsa_block_scores")
+    return scores
+
+
+def qsa_block_topk(scores: torch.Tensor, k: int, ids: torch.Tensor | None = None) -> torch.Tensor:
+    """Rank-ordered top-k block ids [nq, k] (int32, -1 padded) of scores [nq, active_blocks]."""
+    _require_gpu_f32("scores", scores, 2)
+    nq, a = scores.shape
+    k = int(k)
+    if ids is None:
+        ids = torch.empty((nq, max(k, 0)), dtype=torch.int32, device=scores.device)
+    elif (ids.dtype != torch.int32 or tuple(ids.shape) != (nq, k) or not ids.is_contiguous()
+          or ids.device != scores.device):
+        raise ValueError(f"ids must be a contiguous int32 [{nq}, {k}] tensor on scores' device")
+    with torch.cuda.device(scores.device):
+        st = load_library().qsa_block_topk(scores.data_ptr() if a else None, nq, a, k,
+                                           ids.data_ptr() if ids.numel() else None,
+                                           _stream_handle(scores.device))
+    if st != QSA_OK:
+        raise QSAError(st, "qsa_block_topk")
+    return ids
+
+
+# Short aliases.
+block_scores = qsa_block_scores
+block_topk = qsa_block_topk

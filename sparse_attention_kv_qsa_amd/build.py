@@ -1,0 +1,47 @@
+"""Build libqsa.so for gfx950 with hipcc (in-tree, next to this file).
+
+    python -m sparse_attention_kv_qsa_amd.build
+
+Cross-compiles on a host without a GPU.  Packed-fp32 instructions are switched
+off for all device code (``-Xclang -target-feature -Xclang -packed-fp32-ops``);
+hipcc's host pass warns that it does not know that feature, which is harmless.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_PATH = os.path.join(PKG, "libqsa.so")
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def sources() -> list[str]:
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB_PATH) -> str:
+    """Compile every csrc/*.hip into one shared library; returns its path."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = out + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, *(extra or []), f"-I{INCLUDE}", f"-I{CSRC}", *sources(), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True, extra=sys.argv[1:]))

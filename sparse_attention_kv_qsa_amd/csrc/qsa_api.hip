@@ -1,0 +1,63 @@
+// C ABI of libqsa.so (declared in include/qsa.h): argument checks, then the
+// launches.  Every check happens before anything is enqueued, so a rejected
+// call has no effect on the stream.
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "qsa.h"
+#include "qsa_internal.h"
+
+static_assert(QSA_TOPK_MAX_K == qsa::kTopkMaxK, "header and kernels disagree on the top-k limit");
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" int qsa_block_scores(const float *q, const float *kblk, int nq, int heads, int dim,
+                                int active_blocks, float *scores, void *stream) {
+  if (nq < 0 || heads < 0 || dim < 0 || active_blocks < 0) return QSA_ERR_SHAPE;
+  const int64_t K = int64_t(heads) * dim;
+  if (K < 4 || K % 4 != 0 || K > QSA_MAX_HEAD_DIM) return QSA_ERR_SHAPE;
+  if (nq == 0 || active_blocks == 0) return QSA_OK;
+  if (!q || !kblk || !scores) return QSA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(kblk, 16) || !aligned(scores, 4)) return QSA_ERR_ALIGN;
+  (void)hipGetLastError();  // start from a clean launch status
+  return launch_status(qsa::launch_block_scores(q, kblk, nq, int(K), active_blocks, scores,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int qsa_block_topk(const float *scores, int nq, int active_blocks, int k, int *ids,
+                              void *stream) {
+  if (nq < 0 || active_blocks < 0) return QSA_ERR_SHAPE;
+  if (k < 0 || k > QSA_TOPK_MAX_K) return QSA_ERR_K;
+  if (nq == 0 || k == 0) return QSA_OK;
+  if (!ids || (active_blocks > 0 && !scores)) return QSA_ERR_NULL;
+  if (!aligned(ids, 4) || !aligned(scores, 4)) return QSA_ERR_ALIGN;
+  (void)hipGetLastError();
+  return launch_status(qsa::launch_block_topk(scores, nq, active_blocks, k, ids,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+extern "C" const char *qsa_strerror(int status) {
+  switch (status) {
+    case QSA_OK:
+      return "success";
+    case QSA_ERR_NULL:
+      return "a required pointer is NULL";
+    case QSA_ERR_SHAPE:
+      return "bad shape: a size is negative, or heads*dim is not a multiple of 4 in [4, 4096]";
+    case QSA_ERR_K:
+      return "bad k: k < 0 or k > 4096";
+    case QSA_ERR_ALIGN:
+      return "misaligned pointer: q/kblk need 16 bytes, scores/ids 4 bytes";
+    case QSA_ERR_LAUNCH:
+      return "the HIP runtime rejected a kernel launch";
+    default:
+      return "unknown status";
+  }
+}
