@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Throughput of the QSA selection hot path (block scores + top-k) on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one full selection pass over one batch of synthetic input:
+qsa_block_scores then qsa_block_topk, through the C ABI, on the current torch
+stream.  Default workload: 256 prompt queries x 32,770 active blocks (a 131K
+context) in a 65,538-block (262,144-cell) capacity, 4 heads x 128, k = 512.
+
+Steps rotate over several input copies (different HBM buffers, same values) so
+that the block summaries read by each step are not still sitting in the 256 MB
+last-level cache from the previous one.  Inputs are resident in HBM before the
+timed region starts.  Prints ONE JSON line.
+
+Per-kernel durations come from HIP events recorded on the stream the kernels
+run on, around each launch inside the timed region; `roofline` reports the
+scorer (the dominant kernel) against the fp32 matrix-core peak using the
+algorithmic FLOP count 2 * nq * A * heads * dim.
+
+The CPU baseline is the CPU oracle (FP64 scores, then a sort-based top-k of its
+fp32-rounded scores) timed on this host's cores over the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from sparse_attention_kv_qsa_amd import synth  # noqa: E402
+
+METRIC = "QSA select ms/call (score+top-k), 256q x 131K ctx; queries*blocks/s; % roofline"
+UNIT = "queries*blocks/s"
+# MI355X published dense peaks.
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+# The pages' standalone figure for this workload (R9700, gfx1201): scores
+# 0.65 ms + top-k 0.51 ms per call at 256 queries, 131K context.  Context only.
+PAGES_SELECT_MS = 0.65 + 0.51
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scores_mfma_prompt-128k.txt")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=synth.HEADLINE, choices=list(synth.WORKLOADS))
+    p.add_argument("--copies", type=int, default=6,
+                   help="input copies rotated over the steps (defeats cache reuse)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-threads", type=int, default=16)
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="only run a plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("qsa_scores.hip", "qsa_internal.h"):
+        with open(os.path.join(ROOT, "sparse_attention_kv_qsa_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per scorer launch from committed counter runs, if they were
+    taken on the current scorer source; else None."""
+    if workload != synth.HEADLINE or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("scorer_source_sha256_16") != source_digest():
+        return None
+    try:
+        return int(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w: synth.Workload, bt: synth.Batch, threads: int):
+    """Time the CPU oracle on all queries of the workload, `passes` times."""
+    import oracle
+
+    orc = oracle.default()
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = max(1, min(threads, avail or 1))
+    chunks = np.array_split(np.arange(w.nq), threads)
+
+    def run(rows):
+        if len(rows) == 0:
+            return
+        s64 = orc.scores_f64(bt.q[rows], bt.kblk, w.active)
+        orc.topk(s64.astype(np.float32), w.k)
+
+    passes, rates = 3, []
+    with cf.ThreadPoolExecutor(threads) as ex:
+        for _ in range(passes):
+            t0 = time.perf_counter()
+            list(ex.map(run, chunks))
+            dt = time.perf_counter() - t0
+            rates.append(w.nq * w.active / dt)
+    return {
+        "value": float(np.median(rates)),
+        "unit": UNIT,
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"all {w.nq} queries x {w.active} blocks of {w.name} (FP64 scores + sort "
+                   f"top-k of the fp32-rounded scores), {passes} passes, median; "
+                   f"{threads} threads over query rows"),
+    }
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the selection path "
+                          "is not sharded across GPUs here (see the design notes)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    from sparse_attention_kv_qsa_amd import binding, qsa_block_scores, qsa_block_topk
+
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n * 4, "launches": 3}))
+        return
+
+    w = synth.WORKLOADS[args.workload]
+    bt = synth.make_batch(w)
+    ncopy = max(1, args.copies)
+    q_d = [torch.from_numpy(bt.q).to(dev) for _ in range(ncopy)]
+    k_d = [torch.from_numpy(bt.kblk).to(dev) for _ in range(ncopy)]
+    s_d = [torch.empty((w.nq, w.active), dtype=torch.float32, device=dev) for _ in range(ncopy)]
+    i_d = [torch.empty((w.nq, w.k), dtype=torch.int32, device=dev) for _ in range(ncopy)]
+    torch.cuda.synchronize()
+
+    def step(c):
+        qsa_block_scores(q_d[c], k_d[c], w.active, scores=s_d[c])
+        qsa_block_topk(s_d[c], w.k, ids=i_d[c])
+
+    for it in range(args.warmup):
+        step(it % ncopy)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for it in range(K):
+        c = it % ncopy
+        e0, e1, e2 = ev[it]
+        e0.record()
+        qsa_block_scores(q_d[c], k_d[c], w.active, scores=s_d[c])
+        e1.record()
+        qsa_block_topk(s_d[c], w.k, ids=i_d[c])
+        e2.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    score_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    topk_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    ms_step = wall * 1e3 / K
+    value = w.nq * w.active / (wall / K)
+
+    flop = 2.0 * w.nq * w.active * w.K
+    score_avg_s = float(np.mean(score_ms)) * 1e-3
+    achieved = flop / score_avg_s / 1e12
+    mfma_bound = w.nq > 8
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
+                "traffic": read_traffic(w.name)}
+    else:
+        nbytes = 4.0 * (w.active * w.K + w.nq * w.K + w.nq * w.active)
+        gbs = nbytes / score_avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    topk_bytes = 4.0 * (w.nq * w.active + w.nq * w.k)
+    topk_avg_s = float(np.mean(topk_ms)) * 1e-3
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (round(value / (256 * 32770 / (PAGES_SELECT_MS * 1e-3)), 3)
+                        if w.name == synth.HEADLINE else None),
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) fp32 queries and block summaries, planted needles)",
+        "config": {
+            "workload": (f"{w.name}: {w.nq} queries x {w.active} active blocks "
+                         f"({w.capacity}-block capacity), {w.heads} heads x {w.dim}, k={w.k}"),
+            "nq": w.nq, "active_blocks": w.active, "capacity_blocks": w.capacity,
+            "heads": w.heads, "dim": w.dim, "k": w.k, "input_copies": ncopy,
+        },
+        "stages": {
+            "scores_ms": round(float(np.mean(score_ms)), 5),
+            "scores_ms_median": round(float(np.median(score_ms)), 5),
+            "topk_ms": round(float(np.mean(topk_ms)), 5),
+            "topk_ms_median": round(float(np.median(topk_ms)), 5),
+            "topk_gbs": round(topk_bytes / topk_avg_s / 1e9, 1),
+            "topk_hbm_frac": round(topk_bytes / topk_avg_s / 1e9 / PEAK_HBM_GBS, 4),
+        },
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, bt, args.cpu_threads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
