@@ -17,6 +17,8 @@
 // so identical summaries give bitwise-identical scores.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -101,45 +103,65 @@ __global__ __launch_bounds__(256) void scores_gemv_kernel(const float *__restric
 // of 4 consecutive K elements of its row; MFMA step c of an iteration takes
 // component c, so one iteration covers 16 K elements: lane group g (= l/16)
 // contributes elements kk + 4g + c.  A and B use the same assignment, so the
-// contraction is exact in which products meet; only the fp32 rounding order
-// is fixed by it.
+// contraction pairs the right products; only the fp32 rounding order is fixed
+// by it.
+//
+// Loads are raw buffer loads whose resource covers just the tile's valid rows:
+// the hardware returns zeros for rows past nq or past the active blocks, and
+// for K elements outside the wave's quarter the offset is pushed out of range.
+// Zero operands add exact zeros, so a tile's ragged edge runs the same
+// instruction stream as a full tile and every score is computed the same way
+// wherever its block sits.  Iterations alternate between two register sets,
+// so the loads for the next 16 K elements are in flight while the MFMAs of
+// the current ones issue.
 // ---------------------------------------------------------------------------
-constexpr int TM = 64;   // queries per tile
-constexpr int TN = 64;   // blocks per tile
+constexpr int TM = 64;       // queries per tile
+constexpr int TN = 64;       // blocks per tile
 constexpr int PSTRIDE = 68;  // LDS row stride of a partial tile (bank spread)
+constexpr uint32_t kOutOfRange = 0x40000000u;  // byte offset past any tile resource
 
 __device__ __forceinline__ f4 mfma16x16x4(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const float *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, int(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ f4 buffer_f4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// One 64 x 64 output tile.  FULL: all 64 block rows are active.  A ragged last
+// tile (FULL = false) skips the 16-block sub-tiles that hold no active block;
+// the sub-tiles it does run execute the same instruction stream as in a full
+// tile, so every score is bitwise the same wherever its block sits.
 template <bool FULL>
-__device__ __forceinline__ void mfma_tile_body(const float *__restrict__ q,
-                                               const float *__restrict__ kblk, int nq, int K,
-                                               int A, int q0, int b0, int wave, int lane,
-                                               float (*part)[TM][PSTRIDE]) {
+__device__ __forceinline__ void score_tile(const float *__restrict__ q,
+                                           const float *__restrict__ kblk, int nq, int K, int A,
+                                           float *__restrict__ scores, int q0, int b0,
+                                           float (*part)[TM][PSTRIDE]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int g = lane >> 4;
+  const int nni = FULL ? 4 : min(4, (A - b0 + 15) / 16);  // sub-tiles with an active block
+
+  const uint32_t row_bytes = uint32_t(K) * 4u;
+  const __amdgpu_buffer_rsrc_t rq = tile_rsrc(q + int64_t(q0) * K, uint32_t(min(TM, nq - q0)) * row_bytes);
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kblk + int64_t(b0) * K, uint32_t(min(TN, A - b0)) * row_bytes);
+
   const int KQ = ((K + 15) / 16) * 4;  // quarter of K, rounded up to a multiple of 4
   const int kbeg = wave * KQ;
   const int kend = min(K, kbeg + KQ);
-  // Sub-tiles along N that hold at least one active block (all 4 when FULL).
-  const int nni = FULL ? 4 : min(4, (A - b0 + 15) / 16);
 
-  const float *qrow[4];
-  const float *krow[4];
-  bool qok[4], kok[4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const int qi = q0 + 16 * mi + r16;
-    qok[mi] = qi < nq;
-    qrow[mi] = q + int64_t(qok[mi] ? qi : 0) * K;
-  }
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int bj = b0 + 16 * ni + r16;
-    kok[ni] = FULL || bj < A;
-    krow[ni] = kblk + int64_t(kok[ni] ? bj : 0) * K;
-  }
+  // Byte offset of this lane's float4 at iteration base kk (row part added per sub-tile).
+  auto koff = [&](int kk) -> uint32_t {
+    const int e = kk + 4 * g;
+    return e < kend ? uint32_t(e) * 4u : kOutOfRange;
+  };
+  const uint32_t rowoff = uint32_t(r16) * row_bytes;
+  const uint32_t sub = 16u * row_bytes;  // byte stride between 16-row sub-tiles
 
   f4 acc[4][4];
 #pragma unroll
@@ -147,22 +169,15 @@ __device__ __forceinline__ void mfma_tile_body(const float *__restrict__ q,
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f4{0.f, 0.f, 0.f, 0.f};
 
-  const f4 zero = {0.f, 0.f, 0.f, 0.f};
-  f4 a[4], b[4], an[4], bn[4];
-  auto load = [&](f4 *aa, f4 *bb, int kk) {
-    const int e = kk + 4 * g;
-    const bool kin = e < kend;
+  auto load = [&](f4 *a, f4 *b, int kk) {
+    const uint32_t o = koff(kk) + rowoff;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) aa[mi] = (kin && qok[mi]) ? load_f4(qrow[mi] + e) : zero;
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-      bb[ni] = (kin && kok[ni] && (FULL || ni < nni)) ? load_f4(krow[ni] + e) : zero;
+    for (int i = 0; i < 4; ++i) {
+      a[i] = buffer_f4(rq, o + uint32_t(i) * sub);
+      if (FULL || i < nni) b[i] = buffer_f4(rk, o + uint32_t(i) * sub);
+    }
   };
-
-  if (kbeg < kend) load(a, b, kbeg);
-  for (int kk = kbeg; kk < kend; kk += 16) {
-    const bool more = kk + 16 < kend;
-    if (more) load(an, bn, kk + 16);
+  auto mma = [&](const f4 *a, const f4 *b) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -170,13 +185,17 @@ __device__ __forceinline__ void mfma_tile_body(const float *__restrict__ q,
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
           if (FULL || ni < nni) acc[mi][ni] = mfma16x16x4(a[mi][c], b[ni][c], acc[mi][ni]);
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = an[i];
-        b[i] = bn[i];
-      }
-    }
+  };
+
+  // Ping-pong over 16-element steps; a step past kend loads zeros (no memory
+  // access) and its MFMAs add exact zeros.
+  f4 a0[4], b0v[4], a1[4], b1v[4];
+  load(a0, b0v, kbeg);
+  for (int kk = kbeg; kk < kend; kk += 32) {
+    load(a1, b1v, kk + 16);
+    mma(a0, b0v);
+    load(a0, b0v, kk + 32);
+    mma(a1, b1v);
   }
 
 #pragma unroll
@@ -185,29 +204,6 @@ __device__ __forceinline__ void mfma_tile_body(const float *__restrict__ q,
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int r = 0; r < 4; ++r) part[wave][16 * mi + 4 * g + r][16 * ni + r16] = acc[mi][ni][r];
-}
-
-// blockIdx -> tile: consecutive workgroup ids go round-robin over the 8 XCDs,
-// so each XCD gets a contiguous run of tiles (query tiles fastest) and the
-// query tiles that share a block tile share that XCD's L2.
-__global__ __launch_bounds__(256, 2) void scores_mfma_kernel(const float *__restrict__ q,
-                                                             const float *__restrict__ kblk,
-                                                             int nq, int K, int A,
-                                                             float *__restrict__ scores,
-                                                             int nqt, int ntiles,
-                                                             int tiles_per_xcd) {
-  __shared__ float part[4][TM][PSTRIDE];
-  const int tile = (blockIdx.x & 7) * tiles_per_xcd + (blockIdx.x >> 3);
-  if (tile >= ntiles) return;  // whole workgroup leaves before any barrier
-  const int q0 = (tile % nqt) * TM;
-  const int b0 = (tile / nqt) * TN;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-
-  if (b0 + TN <= A)
-    mfma_tile_body<true>(q, kblk, nq, K, A, q0, b0, wave, lane, part);
-  else
-    mfma_tile_body<false>(q, kblk, nq, K, A, q0, b0, wave, lane, part);
   __syncthreads();
 
 #pragma unroll 4
@@ -216,6 +212,34 @@ __global__ __launch_bounds__(256, 2) void scores_mfma_kernel(const float *__rest
     const float s = (part[0][i][j] + part[1][i][j]) + (part[2][i][j] + part[3][i][j]);
     if (q0 + i < nq && b0 + j < A) scores[int64_t(q0 + i) * A + b0 + j] = s;
   }
+}
+
+// Tiles are 64 queries x 64 blocks: nqt query tiles by nct block tiles, the
+// last block tile ragged when A is not a multiple of 64 (e.g. the 32,770 =
+// 512 * 64 + 2 blocks of a 131K context).  Workgroup ids go round-robin over
+// the 8 XCDs (XCD = blockIdx % 8), each XCD dispatching its own ids in order.
+// Each XCD gets an equal share of the full tiles (query tiles fastest, so the
+// query tiles of one block tile share that XCD's L2) and every eighth ragged
+// tile; its ragged tiles -- the cheapest -- go first, so no XCD is left with a
+// lone full tile in a last partial round.
+__global__ __launch_bounds__(256, 2) void scores_mfma_kernel(const float *__restrict__ q,
+                                                             const float *__restrict__ kblk,
+                                                             int nq, int K, int A,
+                                                             float *__restrict__ scores,
+                                                             int nqt, int nct, int ntail) {
+  __shared__ float part[4][TM][PSTRIDE];
+  const int x = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int tails_here = ntail > x ? (ntail - x + 7) / 8 : 0;
+  if (slot < tails_here) {
+    const int qt = x + 8 * slot;
+    score_tile<false>(q, kblk, nq, K, A, scores, qt * TM, (nct - 1) * TN, part);
+    return;
+  }
+  const int64_t nfull = int64_t(nqt) * (nct - (ntail > 0 ? 1 : 0));
+  const int64_t f = nfull * x / 8 + (slot - tails_here);
+  if (f >= nfull * (x + 1) / 8) return;  // whole workgroup leaves before any barrier
+  score_tile<true>(q, kblk, nq, K, A, scores, int(f % nqt) * TM, int(f / nqt) * TN, part);
 }
 
 template <int NQ, int NC>
@@ -267,10 +291,14 @@ hipError_t launch_block_scores(const float *q, const float *kblk, int nq, int K,
   }
   const int nqt = (nq + TM - 1) / TM;
   const int nct = (A + TN - 1) / TN;
-  const int ntiles = nqt * nct;
-  const int per_xcd = (ntiles + 7) / 8;
-  scores_mfma_kernel<<<8 * per_xcd, 256, 0, stream>>>(q, kblk, nq, K, A, scores, nqt, ntiles,
-                                                      per_xcd);
+  const int ntail = (A % TN) ? nqt : 0;
+  const int64_t nfull = int64_t(nqt) * (nct - (ntail ? 1 : 0));
+  int64_t per = 0;  // workgroups per XCD: the largest share
+  for (int x = 0; x < 8; ++x) {
+    const int64_t tails = ntail > x ? (ntail - x + 7) / 8 : 0;
+    per = std::max(per, tails + nfull * (x + 1) / 8 - nfull * x / 8);
+  }
+  scores_mfma_kernel<<<int(8 * per), 256, 0, stream>>>(q, kblk, nq, K, A, scores, nqt, nct, ntail);
   return hipGetLastError();
 }
 

@@ -6,22 +6,27 @@
 // the number of blocks); "#337 hip: gfx12 (RDNA4) QSA select ...", What item 1
 // (the width follows the ACTIVE block count, never the capacity).
 //
-// One workgroup of 1024 threads (16 waves) selects one row.  Steps:
+// One workgroup of 1024 threads (16 waves) selects one row.
 //   1. key transform: fp32 score -> uint32 whose unsigned order is the score
-//      order (-0.0 folded onto +0.0);
-//   2. up to four MSB-first passes over 8-bit digits: a 256-bin LDS histogram
-//      of the candidates still sharing the threshold prefix (one sub-histogram
-//      per wave), a suffix scan to find the bin holding the k-th largest key,
-//      then the prefix grows by that digit.  A pass whose bin is taken whole
-//      ends the search early;
-//   3. if more keys equal the threshold key T than are still needed, the same
-//      passes run over the block id (lowest ids first) among keys == T -- so
-//      ties go to the lower block id;
-//   4. the k winners are gathered into LDS as (key, id) pairs and
-//      bitonic-sorted into rank order: key descending, then id ascending.
-// Keys live in registers, PER per thread plus one slot in LDS (thread t holds
-// ids t + j*1024), PER chosen from the active block count.  Rows longer than
-// the largest width stream their keys from global memory on every pass.
+//      order (-0.0 folded onto +0.0).  Keys live in VGPRs, PER per thread plus
+//      one slot in LDS (thread t holds ids t + j*1024), PER chosen from the
+//      active block count; rows past the largest width stream from memory.
+//   2. a lower bound on the threshold from the threads' own maxima (distinct
+//      elements): each wave sorts its 64 maxima in registers and offers its
+//      ceil(k/16)-th; the smallest offer is <= the k-th largest key.  Only
+//      keys at or above the bound can win; they are compacted into LDS (a few
+//      percent of an N(0,1) row at k/A = 1/64).
+//   3. radix select on the candidates: up to four MSB-first passes over 8-bit
+//      digits, each a 256-bin LDS histogram (one sub-histogram per wave), a
+//      suffix scan to find the bin holding the k-th largest key, and the
+//      prefix grows by that digit; a pass whose bin is taken whole ends early.
+//      If more keys equal the threshold key T than are still needed, the same
+//      passes run over the block id (lowest first) among keys == T, so ties go
+//      to the lower block id.  (If the candidates overflow LDS, the passes run
+//      over the register-resident row instead; the result is the same.)
+//   4. the k winners are gathered into LDS and bitonic-sorted into rank order
+//      (key desc, id asc): in registers with wave shuffles for strides < 64,
+//      through LDS above that.
 #include <hip/hip_runtime.h>
 
 #include "qsa_internal.h"
@@ -32,26 +37,84 @@ namespace {
 constexpr int NT = kTopkThreads;
 constexpr int NWAVES = NT / 64;
 constexpr int MAXK = kTopkMaxK;
+constexpr int CAP = 8192;  // LDS candidate capacity
 
 struct TopkShared {
   uint32_t hsub[NWAVES][256];  // per-wave digit histograms
   uint32_t wtot[4];            // scan carry of the four scanning waves
   uint32_t bcast[3];           // chosen digit, remaining k, count in the bin
-  uint32_t count;              // gathered winners
-  uint32_t extra[NT];          // each thread's last key slot (kept in LDS, not VGPRs)
-  uint32_t bkey[MAXK];         // winners' keys ...
+  uint32_t ncand;              // candidates gathered
+  uint32_t nwin;               // winners gathered
+  uint32_t wmin[NWAVES];       // per-wave candidate bound
+  uint32_t ckey[CAP];          // candidates: keys ...
+  uint32_t cid[CAP];           // ... and block ids
+  uint32_t bkey[MAXK];         // winners: keys ...
   uint32_t bid[MAXK];          // ... and ids, sorted into rank order
+  uint32_t extra[NT];          // each thread's last key slot (kept in LDS, not VGPRs)
 };
 
-// Order-preserving map of an fp32 score to uint32: a larger score gives a
-// larger key.  -0.0 is folded onto +0.0.  Key 0 is kept free as the "no
-// block" sentinel of register slots past the row end; the one score that
-// would map there is a NaN (whose rank is unspecified), so it moves to 1.
-__device__ __forceinline__ uint32_t score_key(float s) {
-  uint32_t u = __float_as_uint(s);
+// Order-preserving map of an fp32 score (given as its bits) to uint32: a
+// larger score gives a larger key.  -0.0 is folded onto +0.0.  Key 0 is kept
+// free as the "no block" sentinel; the one score that would map there is a
+// NaN (whose rank is unspecified), so it moves to 1.
+__device__ __forceinline__ uint32_t score_key(uint32_t u) {
   if (u == 0x80000000u) u = 0u;
   const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return key == 0u ? 1u : key;
+}
+
+// v of lane (lane ^ S) for a power of two S < 64.  Strides up to 8 stay on
+// the VALU (DPP quad permutes, row shifts under bank masks, a row rotate); 16
+// and 32 cross rows through the LDS crossbar.  S must be a compile-time
+// constant after unrolling: a runtime switch here costs a dozen scalar
+// branches per exchange.
+template <int S>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  const int x = int(v);
+  if constexpr (S == 1) {
+    return uint32_t(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+  } else if constexpr (S == 2) {
+    return uint32_t(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+  } else if constexpr (S == 4) {
+    // banks 0 and 2 (lane bit 2 clear) read lane + 4, banks 1 and 3 read lane - 4
+    const int r = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0x5, false);  // row_shl:4
+    return uint32_t(__builtin_amdgcn_update_dpp(r, x, 0x114, 0xF, 0xA, false));  // row_shr:4
+  } else if constexpr (S == 8) {
+    return uint32_t(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));  // row_ror:8
+  } else {
+    return uint32_t(__shfl_xor(x, S, 64));
+  }
+}
+
+// One compare-exchange step of a bitonic network held one element per lane,
+// for a partner in the same wave (STRIDE < 64).  `pos` is the element's
+// position; blocks whose position has the SIZE bit clear run in rank order.
+// Ties (identical pairs) never swap.
+template <int SIZE, int STRIDE, class Before>
+__device__ __forceinline__ void bitonic_lane_step(uint32_t &key, uint32_t &id, int pos,
+                                                  Before &&before) {
+  const uint32_t pk = lane_xor<STRIDE>(key);
+  const uint32_t pi = lane_xor<STRIDE>(id);
+  // Branch-free: both orders are evaluated and selected with bit operations
+  // (a conditional here compiles to divergent branches on every step).
+  const bool take_first = ((pos & STRIDE) == 0) == ((pos & SIZE) == 0);
+  const bool take = (take_first & before(pk, pi, key, id)) | (!take_first & before(key, id, pk, pi));
+  key = take ? pk : key;
+  id = take ? pi : id;
+}
+
+// All steps of stage SIZE with strides below 64 (STRIDE = min(SIZE, 64) / 2 down to 1).
+template <int SIZE, int STRIDE, class Before>
+__device__ __forceinline__ void bitonic_lane_stage(uint32_t &key, uint32_t &id, int pos,
+                                                   Before &&before) {
+  if constexpr (STRIDE >= 1) {
+    bitonic_lane_step<SIZE, STRIDE>(key, id, pos, before);
+    bitonic_lane_stage<SIZE, STRIDE / 2>(key, id, pos, before);
+  }
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
 }
 
 // Given the histogram of the current digit in sh.hsub (complete: the caller
@@ -99,6 +162,180 @@ __device__ __forceinline__ void find_digit(TopkShared &sh, uint32_t sub0, uint32
   cnt = sh.bcast[2];
 }
 
+// Outcome of a radix select: an element (id, key) is a winner iff
+//   (key & mask) >  pref, or
+//   (key & mask) == pref and (!by_id or ((idtop - id) & idmask) >= idpref).
+struct Threshold {
+  uint32_t pref = 0, mask = 0;
+  uint32_t idpref = 0, idmask = 0, idtop = 0;
+  bool by_id = false;
+  __device__ bool wins(uint32_t id, uint32_t key) const {
+    const uint32_t kp = key & mask;
+    const bool id_ok = !by_id | (((idtop - id) & idmask) >= idpref);
+    return (kp > pref) | ((kp == pref) & id_ok);
+  }
+};
+
+// Radix select of the k largest (key, id) pairs among those `visit` yields
+// (key 0 = sentinel; n_sentinel of them among the visited).  k must be less
+// than the number of real keys.  ids are block ids < A.
+template <class Visit>
+__device__ __forceinline__ Threshold radix_select(TopkShared &sh, Visit &&visit, uint32_t k, uint32_t n_sentinel,
+                                  int A) {
+  const int wave = threadIdx.x >> 6;
+  Threshold th;
+  uint32_t kr = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    const uint32_t mask = th.mask, pref = th.pref;
+    visit([&](uint32_t, uint32_t key) {
+      if ((key & mask) == pref) atomicAdd(&sh.hsub[wave][(key >> shift) & 255u], 1u);
+    });
+    __syncthreads();
+    uint32_t d, cnt;
+    find_digit(sh, th.pref == 0 ? n_sentinel : 0u, kr, d, cnt);
+    th.pref |= d << shift;
+    th.mask |= 0xFFu << shift;
+    if (cnt == kr) return th;
+  }
+  // More keys equal T = pref than are still needed: take the kr lowest ids.
+  th.by_id = true;
+  const int idbits = 32 - __clz(uint32_t(A - 1));
+  th.idtop = idbits >= 32 ? 0xFFFFFFFFu : ((1u << idbits) - 1u);
+  for (int shift = 8 * ((idbits + 7) / 8 - 1); shift >= 0; shift -= 8) {
+    const uint32_t T = th.pref, idmask = th.idmask, idpref = th.idpref, idtop = th.idtop;
+    visit([&](uint32_t id, uint32_t key) {
+      const uint32_t rid = idtop - id;
+      if (key == T && (rid & idmask) == idpref) atomicAdd(&sh.hsub[wave][(rid >> shift) & 255u], 1u);
+    });
+    __syncthreads();
+    uint32_t d, cnt;
+    find_digit(sh, 0u, kr, d, cnt);
+    th.idpref |= d << shift;
+    th.idmask |= 0xFFu << shift;
+    if (cnt == kr) break;
+  }
+  return th;
+}
+
+// Append the (id, key) pairs for which pred holds to LDS arrays at
+// counter `*count`, one LDS atomic per wave.  `visit` must visit every lane
+// of the wave the same number of times (all lanes active).  Writes past
+// `cap` are dropped; the counter still counts them.
+template <class Visit, class Pred>
+__device__ __forceinline__ void compact(Visit &&visit, Pred &&pred, uint32_t *count, uint32_t *dkey,
+                        uint32_t *did, uint32_t cap) {
+  const int lane = threadIdx.x & 63;
+  uint32_t total = 0;
+  visit([&](uint32_t id, uint32_t key) { total += __popcll(__ballot(pred(id, key))); });
+  uint32_t base = 0;
+  if (lane == 0 && total) base = atomicAdd(count, total);
+  base = __builtin_amdgcn_readfirstlane(base);
+  visit([&](uint32_t id, uint32_t key) {
+    // Re-evaluate the predicate here rather than keep every slot's wave mask
+    // from the counting visit alive in scalar registers.
+    asm volatile("" : "+v"(key));
+    const bool p = pred(id, key);
+    const uint64_t bal = __ballot(p);
+    const uint32_t pos = base + lanes_below(bal);
+    if (p && pos < cap) {
+      dkey[pos] = key;
+      did[pos] = id;
+    }
+    base += __popcll(bal);
+  });
+}
+
+// Rank-order sort of sh.bkey/bid[0, m) and the store of one row of ids.
+__device__ void sort_and_store(TopkShared &sh, int m, int k, int *__restrict__ orow) {
+  const int t = threadIdx.x;
+  int P = 1;
+  while (P < m) P <<= 1;
+  if (P <= NT) {
+    // One element per thread: strides below 64 exchange inside the wave,
+    // larger strides through LDS.
+    uint32_t key = 0u, id = 0xFFFFFFFFu;  // padding ranks after every winner
+    if (t < m) {
+      key = sh.bkey[t];
+      id = sh.bid[t];
+    }
+    auto rank_before = [](uint32_t ka, uint32_t ia, uint32_t kb, uint32_t ib) {
+      return (ka > kb) | ((ka == kb) & (ia < ib));
+    };
+    auto lds_step = [&](int size, int stride) {
+      __syncthreads();
+      sh.bkey[t] = key;
+      sh.bid[t] = id;
+      __syncthreads();
+      const uint32_t pk = sh.bkey[t ^ stride], pi = sh.bid[t ^ stride];
+      const bool take_first = ((t & stride) == 0) == ((t & size) == 0);
+      const bool take =
+          (take_first & rank_before(pk, pi, key, id)) | (!take_first & rank_before(key, id, pk, pi));
+      key = take ? pk : key;
+      id = take ? pi : id;
+    };
+    // Stages 2..64 run whole inside each wave; later stages start with their
+    // cross-wave strides, then finish with the in-wave ones.
+    if (P >= 2) bitonic_lane_stage<2, 1>(key, id, t, rank_before);
+    if (P >= 4) bitonic_lane_stage<4, 2>(key, id, t, rank_before);
+    if (P >= 8) bitonic_lane_stage<8, 4>(key, id, t, rank_before);
+    if (P >= 16) bitonic_lane_stage<16, 8>(key, id, t, rank_before);
+    if (P >= 32) bitonic_lane_stage<32, 16>(key, id, t, rank_before);
+    if (P >= 64) bitonic_lane_stage<64, 32>(key, id, t, rank_before);
+    if (P >= 128) {
+      lds_step(128, 64);
+      bitonic_lane_stage<128, 32>(key, id, t, rank_before);
+    }
+    if (P >= 256) {
+      lds_step(256, 128);
+      lds_step(256, 64);
+      bitonic_lane_stage<256, 32>(key, id, t, rank_before);
+    }
+    if (P >= 512) {
+      lds_step(512, 256);
+      lds_step(512, 128);
+      lds_step(512, 64);
+      bitonic_lane_stage<512, 32>(key, id, t, rank_before);
+    }
+    if (P >= 1024) {
+      lds_step(1024, 512);
+      lds_step(1024, 256);
+      lds_step(1024, 128);
+      lds_step(1024, 64);
+      bitonic_lane_stage<1024, 32>(key, id, t, rank_before);
+    }
+    if (t < m) orow[t] = int(id);
+    for (int r = m + t; r < k; r += NT) orow[r] = -1;
+    return;
+  }
+  // P in (NT, MAXK]: bitonic network over LDS.
+  __syncthreads();
+  for (int i = m + t; i < P; i += NT) {
+    sh.bkey[i] = 0u;
+    sh.bid[i] = 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int p = t; p < (P >> 1); p += NT) {
+        const int i = ((p & ~(stride - 1)) << 1) | (p & (stride - 1));
+        const int j = i + stride;
+        const uint32_t ki = sh.bkey[i], kj = sh.bkey[j];
+        const uint32_t ii = sh.bid[i], ij = sh.bid[j];
+        const bool j_first = kj > ki || (kj == ki && ij < ii);
+        const bool forward = (i & size) == 0;
+        if (j_first == forward) {
+          sh.bkey[i] = kj;
+          sh.bkey[j] = ki;
+          sh.bid[i] = ij;
+          sh.bid[j] = ii;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int r = t; r < k; r += NT) orow[r] = r < m ? int(sh.bid[r]) : -1;
+}
+
 template <int PER>
 struct RowKeys {
   uint32_t key[PER > 0 ? PER : 1];
@@ -121,142 +358,129 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
   }
 
   for (int i = t; i < NWAVES * 256; i += NT) (&sh.hsub[0][0])[i] = 0;
-  if (t == 0) sh.count = 0;
+  if (t == 0) {
+    sh.ncand = 0;
+    sh.nwin = 0;
+  }
+
+  // Raw buffer loads: the hardware returns 0 past the row end, so every
+  // slot's load is issued unconditionally and in flight together.
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)srow, 0, A * 4, 0x00020000);
+  auto load_key = [&](int id) -> uint32_t {
+    const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(rs, id * 4, 0, 0);
+    return id < A ? score_key(u) : 0u;
+  };
 
   // Thread t owns ids t + j*NT: slots j < PER in VGPRs, slot PER in LDS
   // (sh.extra[t]), so a row of (PER+1)*NT ids needs only PER registers -- the
   // capacity-sized rows of 2^n + 2 blocks spill just two ids into the extra
-  // slot.  Slots past the row end hold the sentinel key 0: it never matches a
-  // threshold (real keys are >= 1), is never gathered, and the n_sentinel of
-  // them are taken out of bin 0 while the prefix is still 0.  This keeps
-  // per-slot validity masks out of the hot loops.
+  // slot.  Slots past the row end hold the sentinel key 0: it never passes
+  // the candidate bound, never matches a threshold (real keys are >= 1), and
+  // the n_sentinel of them are taken out of bin 0 while the prefix is still 0.
   RowKeys<PER> rk;
   uint32_t n_sentinel = 0;
   if constexpr (PER >= 0) {
     n_sentinel = uint32_t((PER + 1) * NT - A);
+    // All loads first (raw bits), then the transform: the empty asm makes each
+    // loaded value live unconditionally, so the compiler cannot sink a load
+    // into the id < A branch and wait on it there.
 #pragma unroll
-    for (int j = 0; j <= PER; ++j) {
-      const int id = j * NT + t;
-      const uint32_t key = id < A ? score_key(srow[id]) : 0u;
-      if (j < PER)
-        rk.key[j < PER ? j : 0] = key;
-      else
-        sh.extra[t] = key;
+    for (int j = 0; j < PER; ++j) rk.key[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, (j * NT + t) * 4, 0, 0);
+    uint32_t xr = __builtin_amdgcn_raw_buffer_load_b32(rs, (PER * NT + t) * 4, 0, 0);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      asm volatile("" : "+v"(rk.key[j]));
+      rk.key[j] = j * NT + t < A ? score_key(rk.key[j]) : 0u;
     }
+    asm volatile("" : "+v"(xr));
+    sh.extra[t] = PER * NT + t < A ? score_key(xr) : 0u;
+  } else {
+    n_sentinel = uint32_t((A + NT - 1) / NT * NT - A);
   }
-  // Visit every (id, key) this thread owns (sentinel slots included).  The
-  // empty asm hides that `tv` equals t, so ids are recomputed in each visit
-  // (one add) instead of being hoisted into PER more live registers.
-  auto for_each = [&](auto &&f) {
+  // Visit every (id, key) this thread owns, sentinel slots included, with all
+  // lanes active.  The empty asm hides that `tv` equals t, so ids are
+  // recomputed in each visit (one add) instead of being hoisted into PER more
+  // live registers; the scheduling barriers keep the compiler from hoisting
+  // every slot's wave-wide masks ahead of their use (scalar-register spills).
+  auto visit_row = [&](auto &&f) {
+    int tv = t;
+    asm volatile("" : "+v"(tv));
     if constexpr (PER >= 0) {
-      int tv = t;
-      asm volatile("" : "+v"(tv));
 #pragma unroll
-      for (int j = 0; j < PER; ++j) f(j * NT + tv, rk.key[j]);
-      f(PER * NT + tv, sh.extra[tv]);
+      for (int j = 0; j < PER; ++j) {
+        f(uint32_t(j * NT + tv), rk.key[j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      f(uint32_t(PER * NT + tv), sh.extra[tv]);
     } else {
-      for (int id = t; id < A; id += NT) f(id, score_key(srow[id]));
+      for (int base = 0; base < A; base += NT) f(uint32_t(base + tv), load_key(base + tv));
     }
   };
   __syncthreads();
 
-  uint32_t pref = 0, mask = 0;      // threshold key prefix and the bits it fixes
-  uint32_t idpref = 0, idmask = 0;  // the same for reversed ids among keys == T
-  uint32_t idtop = 0;               // ids map to rid = idtop - id (larger rid = lower id)
-  bool by_id = false;
-
-  if (k < A) {
-    uint32_t kr = uint32_t(k);
-    bool done = false;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for_each([&](int, uint32_t key) {
-        if ((key & mask) == pref) atomicAdd(&sh.hsub[wave][(key >> shift) & 255u], 1u);
-      });
-      __syncthreads();
-      uint32_t d, cnt;
-      find_digit(sh, pref == 0 ? n_sentinel : 0u, kr, d, cnt);
-      pref |= d << shift;
-      mask |= 0xFFu << shift;
-      if (cnt == kr) {
-        done = true;
-        break;
-      }
+  // Candidate bound.  Every thread's maximum over its own slots is a distinct
+  // element of the row.  Each wave sorts its 64 thread maxima (descending,
+  // lane exchanges only) and takes the kw-th, kw = ceil(k / 16): at least kw
+  // of its maxima are >= it.  The smallest of the 16 wave values is then
+  // exceeded-or-equalled by at least 16 * kw >= k elements, so it is <= the
+  // k-th largest key and every winner lies at or above it.  Without enough
+  // groups (k > 1024) the bound is 1: every real key is a candidate.
+  uint32_t bound = 1u;
+  if (k < A && k <= NT) {
+    uint32_t v = 0u;
+    if constexpr (PER >= 0) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) v = max(v, rk.key[j]);
+      v = max(v, sh.extra[t]);
+    } else {
+      for (int base = 0; base < A; base += NT) v = max(v, load_key(base + t));
     }
-    if (!done) {
-      // More keys equal T = pref than are still needed: take the kr lowest ids.
-      by_id = true;
-      const int idbits = 32 - __clz(uint32_t(A - 1));
-      idtop = idbits >= 32 ? 0xFFFFFFFFu : ((1u << idbits) - 1u);
-      for (int shift = 8 * ((idbits + 7) / 8 - 1); shift >= 0; shift -= 8) {
-        for_each([&](int id, uint32_t key) {
-          const uint32_t rid = idtop - uint32_t(id);
-          if (key == pref && (rid & idmask) == idpref)
-            atomicAdd(&sh.hsub[wave][(rid >> shift) & 255u], 1u);
-        });
-        __syncthreads();
-        uint32_t d, cnt;
-        find_digit(sh, 0u, kr, d, cnt);
-        idpref |= d << shift;
-        idmask |= 0xFFu << shift;
-        if (cnt == kr) break;
-      }
-    }
+    // Wave-local bitonic sort of the 64 maxima, descending (the id slot is unused).
+    auto greater = [](uint32_t ka, uint32_t, uint32_t kb, uint32_t) { return ka > kb; };
+    uint32_t unused = 0u;
+    bitonic_lane_stage<2, 1>(v, unused, lane, greater);
+    bitonic_lane_stage<4, 2>(v, unused, lane, greater);
+    bitonic_lane_stage<8, 4>(v, unused, lane, greater);
+    bitonic_lane_stage<16, 8>(v, unused, lane, greater);
+    bitonic_lane_stage<32, 16>(v, unused, lane, greater);
+    bitonic_lane_stage<64, 32>(v, unused, lane, greater);
+    const int kw = (k + NWAVES - 1) / NWAVES;
+    const uint32_t vw = __builtin_amdgcn_readlane(v, kw - 1);
+    if (lane == 0) sh.wmin[wave] = vw;
+    __syncthreads();
+    uint32_t b = 0xFFFFFFFFu;
+#pragma unroll
+    for (int w = 0; w < NWAVES; ++w) b = min(b, sh.wmin[w]);
+    bound = max(b, 1u);
   }
 
-  // Gather the winners: one LDS atomic per wave and visit.
-  for_each([&](int id, uint32_t key) {
-    const uint32_t kp = key & mask;
-    bool sel = kp > pref;
-    if (kp == pref) sel = !by_id || (((idtop - uint32_t(id)) & idmask) >= idpref);
-    sel = sel && key != 0u;
-    const uint64_t bal = __ballot(sel);
-    if (bal) {
-      const int leader = __ffsll((unsigned long long)bal) - 1;
-      uint32_t base = 0;
-      if (lane == leader) base = atomicAdd(&sh.count, uint32_t(__popcll(bal)));
-      base = __shfl(base, leader, 64);
-      const uint32_t below = __builtin_amdgcn_mbcnt_hi(uint32_t(bal >> 32),
-                                                       __builtin_amdgcn_mbcnt_lo(uint32_t(bal), 0u));
-      if (sel && base + below < uint32_t(MAXK)) {  // exactly m <= MAXK are selected
-        sh.bkey[base + below] = key;
-        sh.bid[base + below] = uint32_t(id);
-      }
-    }
-  });
-
-  int P = 1;
-  while (P < m) P <<= 1;
+  compact(visit_row, [&](uint32_t, uint32_t key) { return key >= bound; }, &sh.ncand, sh.ckey,
+          sh.cid, CAP);
   __syncthreads();
-  for (int i = m + t; i < P; i += NT) {  // padding ranks after every winner
-    sh.bkey[i] = 0u;
-    sh.bid[i] = 0xFFFFFFFFu;
+  const uint32_t C = sh.ncand;
+
+  if (C <= uint32_t(CAP)) {
+    // Select among the LDS candidates (all of them when k >= C).
+    const uint32_t padC = (C + NT - 1) / NT * NT;
+    auto visit_cand = [&](auto &&f) {
+      for (uint32_t i = t; i < padC; i += NT) {
+        const bool ok = i < C;
+        f(ok ? sh.cid[i] : 0u, ok ? sh.ckey[i] : 0u);
+      }
+    };
+    Threshold th;
+    if (uint32_t(k) < C) th = radix_select(sh, visit_cand, uint32_t(k), padC - C, A);
+    compact(visit_cand, [&](uint32_t id, uint32_t key) { return key != 0u && th.wins(id, key); },
+            &sh.nwin, sh.bkey, sh.bid, MAXK);
+  } else {
+    // Too many candidates for LDS: select over the whole row.
+    const Threshold th = radix_select(sh, visit_row, uint32_t(k), n_sentinel, A);
+    compact(visit_row, [&](uint32_t id, uint32_t key) { return key != 0u && th.wins(id, key); },
+            &sh.nwin, sh.bkey, sh.bid, MAXK);
   }
   __syncthreads();
-
-  // Bitonic sort of [0, P) into rank order.  "x before y" is the strict
-  // total order key desc, id asc; a block of the network whose index has the
-  // `size` bit clear sorts forward, otherwise backward.
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int p = t; p < (P >> 1); p += NT) {
-        const int i = ((p & ~(stride - 1)) << 1) | (p & (stride - 1));
-        const int j = i + stride;
-        const uint32_t ki = sh.bkey[i], kj = sh.bkey[j];
-        const uint32_t ii = sh.bid[i], ij = sh.bid[j];
-        const bool j_first = kj > ki || (kj == ki && ij < ii);
-        const bool forward = (i & size) == 0;
-        if (j_first == forward) {
-          sh.bkey[i] = kj;
-          sh.bkey[j] = ki;
-          sh.bid[i] = ij;
-          sh.bid[j] = ii;
-        }
-      }
-      __syncthreads();
-    }
-  }
-
-  for (int r = t; r < k; r += NT) orow[r] = r < m ? int(sh.bid[r]) : -1;
+  sort_and_store(sh, m, k, orow);
 }
 
 template <int PER>
