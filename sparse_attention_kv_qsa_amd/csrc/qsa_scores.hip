@@ -95,7 +95,8 @@ __global__ __launch_bounds__(256) void scores_gemv_kernel(const float *__restric
 // MFMA scorer.  A workgroup (4 waves) owns a 64-query x 64-block output tile.
 // Wave w accumulates the tile over the w-th quarter of K (with heads = 4 that
 // is exactly head w), as 4x4 sub-tiles of v_mfma_f32_16x16x4_f32.  The four
-// partial tiles meet in LDS and are summed as (p0 + p1) + (p2 + p3).
+// partial tiles are summed as (p0 + p1) + (p2 + p3) through two pairwise
+// exchanges in LDS.
 //
 // Operand layout of v_mfma_f32_16x16x4_f32 (wave64): lane l supplies
 // A[row l%16][k l/16] and B[k l/16][col l%16]; the 16x16 result sits in lane
@@ -117,7 +118,6 @@ __global__ __launch_bounds__(256) void scores_gemv_kernel(const float *__restric
 // ---------------------------------------------------------------------------
 constexpr int TM = 64;       // queries per tile
 constexpr int TN = 64;       // blocks per tile
-constexpr int PSTRIDE = 68;  // LDS row stride of a partial tile (bank spread)
 constexpr uint32_t kOutOfRange = 0x40000000u;  // byte offset past any tile resource
 
 __device__ __forceinline__ f4 mfma16x16x4(float a, float b, f4 c) {
@@ -132,6 +132,44 @@ __device__ __forceinline__ f4 buffer_f4(__amdgpu_buffer_rsrc_t r, uint32_t off) 
   return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// Epilogue of one wave of a tile (see score_tile).  W is the wave index.
+template <int W>
+__device__ __forceinline__ void combine_store(const f4 (&acc)[4][4], f4 *xbuf,
+                                              float *__restrict__ scores, int nq, int A, int q0,
+                                              int b0, int lane) {
+  constexpr int keep1 = (W & 1) ? 2 : 0;  // row blocks kept after stage 1: keep1, keep1 + 1
+  constexpr int send1 = 2 - keep1;
+  constexpr int keep2 = (W >> 1) & 1;     // which of the two stays after stage 2
+  constexpr int mi = keep1 + keep2;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) xbuf[((W * 2 + m) * 4 + ni) * 64 + lane] = acc[send1 + m][ni];
+  __syncthreads();
+  f4 half[2][4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+      half[m][ni] = acc[keep1 + m][ni] + xbuf[(((W ^ 1) * 2 + m) * 4 + ni) * 64 + lane];
+  f4 *x2 = xbuf + 4 * 2 * 4 * 64;
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) x2[(W * 4 + ni) * 64 + lane] = half[1 - keep2][ni];
+  __syncthreads();
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const f4 v = half[keep2][ni] + x2[((W ^ 2) * 4 + ni) * 64 + lane];
+    const int col = b0 + 16 * ni + r16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = q0 + 16 * mi + 4 * g + r;
+      if (row < nq && col < A) scores[int64_t(row) * A + col] = v[r];
+    }
+  }
+}
+
 // One 64 x 64 output tile.  FULL: all 64 block rows are active.  A ragged last
 // tile (FULL = false) skips the 16-block sub-tiles that hold no active block;
 // the sub-tiles it does run execute the same instruction stream as in a full
@@ -140,7 +178,7 @@ template <bool FULL>
 __device__ __forceinline__ void score_tile(const float *__restrict__ q,
                                            const float *__restrict__ kblk, int nq, int K, int A,
                                            float *__restrict__ scores, int q0, int b0,
-                                           float (*part)[TM][PSTRIDE]) {
+                                           f4 *xbuf) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
@@ -198,19 +236,21 @@ __device__ __forceinline__ void score_tile(const float *__restrict__ q,
     mma(a1, b1v);
   }
 
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) part[wave][16 * mi + 4 * g + r][16 * ni + r16] = acc[mi][ni][r];
-  __syncthreads();
-
-#pragma unroll 4
-  for (int e = threadIdx.x; e < TM * TN; e += 256) {
-    const int i = e / TN, j = e % TN;
-    const float s = (part[0][i][j] + part[1][i][j]) + (part[2][i][j] + part[3][i][j]);
-    if (q0 + i < nq && b0 + j < A) scores[int64_t(q0 + i) * A + b0 + j] = s;
+  // Combine the four quarter partials as (p0 + p1) + (p2 + p3) in two
+  // pairwise exchanges through LDS (float4 per lane, one 1 KB row of lanes
+  // per access, conflict-free); fp32 addition is commutative, so which wave
+  // of a pair adds does not change a bit.
+  //   stage 1, pairs (0,1) and (2,3): the even wave keeps row blocks 0-1 and
+  //            sends 2-3, the odd wave the reverse -> p0+p1 / p2+p3 halves;
+  //   stage 2, pairs (0,2) and (1,3): each keeps one row block -> the sum.
+  // Wave w ends with row block {0, 2, 1, 3}[w] and stores it from registers.
+  // The wave's role is a template argument so every register-array index is
+  // a compile-time constant (a runtime index would demote acc to scratch).
+  switch (wave) {
+    case 0: combine_store<0>(acc, xbuf, scores, nq, A, q0, b0, lane); break;
+    case 1: combine_store<1>(acc, xbuf, scores, nq, A, q0, b0, lane); break;
+    case 2: combine_store<2>(acc, xbuf, scores, nq, A, q0, b0, lane); break;
+    default: combine_store<3>(acc, xbuf, scores, nq, A, q0, b0, lane); break;
   }
 }
 
@@ -222,24 +262,24 @@ __device__ __forceinline__ void score_tile(const float *__restrict__ q,
 // query tiles of one block tile share that XCD's L2) and every eighth ragged
 // tile; its ragged tiles -- the cheapest -- go first, so no XCD is left with a
 // lone full tile in a last partial round.
-__global__ __launch_bounds__(256, 2) void scores_mfma_kernel(const float *__restrict__ q,
+__global__ __launch_bounds__(256, 3) void scores_mfma_kernel(const float *__restrict__ q,
                                                              const float *__restrict__ kblk,
                                                              int nq, int K, int A,
                                                              float *__restrict__ scores,
                                                              int nqt, int nct, int ntail) {
-  __shared__ float part[4][TM][PSTRIDE];
+  __shared__ f4 xbuf[(4 * 2 * 4 + 4 * 4) * 64];  // 48 KB: three workgroups fit a CU
   const int x = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int tails_here = ntail > x ? (ntail - x + 7) / 8 : 0;
   if (slot < tails_here) {
     const int qt = x + 8 * slot;
-    score_tile<false>(q, kblk, nq, K, A, scores, qt * TM, (nct - 1) * TN, part);
+    score_tile<false>(q, kblk, nq, K, A, scores, qt * TM, (nct - 1) * TN, xbuf);
     return;
   }
   const int64_t nfull = int64_t(nqt) * (nct - (ntail > 0 ? 1 : 0));
   const int64_t f = nfull * x / 8 + (slot - tails_here);
   if (f >= nfull * (x + 1) / 8) return;  // whole workgroup leaves before any barrier
-  score_tile<true>(q, kblk, nq, K, A, scores, int(f % nqt) * TM, int(f / nqt) * TN, part);
+  score_tile<true>(q, kblk, nq, K, A, scores, int(f % nqt) * TM, int(f / nqt) * TN, xbuf);
 }
 
 template <int NQ, int NC>
