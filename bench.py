@@ -15,8 +15,11 @@ timed region starts.  Prints ONE JSON line.
 
 Per-kernel durations come from HIP events recorded on the stream the kernels
 run on, around each launch inside the timed region; `roofline` reports the
-scorer (the dominant kernel) against the fp32 matrix-core peak using the
-algorithmic FLOP count 2 * nq * A * heads * dim.
+scorer (the dominant kernel) against the peak of the matrix-core type it
+runs on: fp32 MFMA with 2 * nq * A * heads * dim FLOP, or -- the default for
+prompts -- bf16 MFMA on the exact three-way split, whose method forms six bf16
+slice products per fp32 product (6 * 2 * nq * A * heads * dim FLOP); the
+fp32-equivalent rate is reported beside it.
 
 The CPU baseline is the CPU oracle (FP64 scores, then a sort-based top-k of its
 fp32-rounded scores) timed on this host's cores over the same workload.
@@ -41,11 +44,17 @@ METRIC = "QSA select ms/call (score+top-k), 256q x 131K ctx; queries*blocks/s; %
 UNIT = "queries*blocks/s"
 # MI355X published dense peaks.
 PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 # The pages' standalone figure for this workload (R9700, gfx1201): scores
 # 0.65 ms + top-k 0.51 ms per call at 256 queries, 131K context.  Context only.
 PAGES_SELECT_MS = 0.65 + 0.51
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_scores_mfma_prompt-128k.txt")
+CSRC = os.path.join(ROOT, "sparse_attention_kv_qsa_amd", "csrc")
+# Scorer kernel per precision path: (source file, counter summary under profiles/).
+SCORERS = {
+    "fp32": ("qsa_scores.hip", "traffic_scores_mfma_prompt-128k.txt"),
+    "bf16x3": ("qsa_scores_bf16x3.hip", "traffic_scores_bf16x3_prompt-128k.txt"),
+}
 
 
 def parse_args():
@@ -56,6 +65,8 @@ def parse_args():
     p.add_argument("--workload", default=synth.HEADLINE, choices=list(synth.WORKLOADS))
     p.add_argument("--copies", type=int, default=6,
                    help="input copies rotated over the steps (defeats cache reuse)")
+    p.add_argument("--scores-mode", default="auto", choices=["auto", "fp32", "bf16x3"],
+                   help="precision mode of qsa_block_scores_ex (auto = the library default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-threads", type=int, default=16)
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -63,26 +74,28 @@ def parse_args():
     return p.parse_args()
 
 
-def source_digest() -> str:
+def source_digest(path: str) -> str:
     import hashlib
     h = hashlib.sha256()
-    for name in ("qsa_scores.hip", "qsa_internal.h"):
-        with open(os.path.join(ROOT, "sparse_attention_kv_qsa_amd", "csrc", name), "rb") as f:
+    for name in (path, "qsa_internal.h"):
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
+def read_traffic(path: str, workload: str):
     """HBM bytes per scorer launch from committed counter runs, if they were
-    taken on the current scorer source; else None."""
-    if workload != synth.HEADLINE or not os.path.exists(TRAFFIC_FILE):
+    taken on the current source of that scorer; else None."""
+    src, summary = SCORERS[path]
+    fname = os.path.join(ROOT, "profiles", summary)
+    if workload != synth.HEADLINE or not os.path.exists(fname):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(fname):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             kv[key.strip()] = val.strip()
-    if kv.get("scorer_source_sha256_16") != source_digest():
+    if kv.get("scorer_source_sha256_16") != source_digest(src):
         return None
     try:
         return int(kv["hbm_bytes_per_launch"])
@@ -134,7 +147,7 @@ def main():
 
     import torch
 
-    from sparse_attention_kv_qsa_amd import binding, qsa_block_scores, qsa_block_topk
+    from sparse_attention_kv_qsa_amd import binding, qsa_block_scores_ex, qsa_block_topk
 
     binding.load_library()
     dev = torch.device("cuda:0")
@@ -159,8 +172,10 @@ def main():
     i_d = [torch.empty((w.nq, w.k), dtype=torch.int32, device=dev) for _ in range(ncopy)]
     torch.cuda.synchronize()
 
+    mode = args.scores_mode
+
     def step(c):
-        qsa_block_scores(q_d[c], k_d[c], w.active, scores=s_d[c])
+        qsa_block_scores_ex(q_d[c], k_d[c], w.active, scores=s_d[c], mode=mode)
         qsa_block_topk(s_d[c], w.k, ids=i_d[c])
 
     for it in range(args.warmup):
@@ -175,7 +190,7 @@ def main():
         c = it % ncopy
         e0, e1, e2 = ev[it]
         e0.record()
-        qsa_block_scores(q_d[c], k_d[c], w.active, scores=s_d[c])
+        qsa_block_scores_ex(q_d[c], k_d[c], w.active, scores=s_d[c], mode=mode)
         e1.record()
         qsa_block_topk(s_d[c], w.k, ids=i_d[c])
         e2.record()
@@ -187,19 +202,33 @@ def main():
     ms_step = wall * 1e3 / K
     value = w.nq * w.active / (wall / K)
 
-    flop = 2.0 * w.nq * w.active * w.K
+    flop = 2.0 * w.nq * w.active * w.K  # fp32-equivalent FLOP of the scores
     score_avg_s = float(np.mean(score_ms)) * 1e-3
-    achieved = flop / score_avg_s / 1e12
-    mfma_bound = w.nq > 8
-    if mfma_bound:
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
-                "traffic": read_traffic(w.name)}
+    # The kernel the library runs for this shape and mode (mirrors its dispatch).
+    if w.nq <= 8 and mode != "bf16x3":
+        path = "gemv"
     else:
+        path = "bf16x3" if mode in ("auto", "bf16x3") else "fp32"
+    extra = {}
+    if path == "gemv":
         nbytes = 4.0 * (w.active * w.K + w.nq * w.K + w.nq * w.active)
         gbs = nbytes / score_avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    elif path == "fp32":
+        tf = flop / score_avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_MFMA_TFLOPS, 4),
+                "traffic": read_traffic("fp32", w.name)}
+    else:
+        # The split method forms six bf16 slice products per fp32 product: its
+        # algorithmic work on the bf16 matrix cores is 6 * 2 * nq * A * K.
+        tf = 6.0 * flop / score_avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_MFMA_TFLOPS, 4),
+                "traffic": read_traffic("bf16x3", w.name)}
+        extra = {"scores_fp32_equiv_tflops": round(flop / score_avg_s / 1e12, 2),
+                 "scores_frac_of_fp32_mfma_peak": round(flop / score_avg_s / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)}
     topk_bytes = 4.0 * (w.nq * w.active + w.nq * w.k)
     topk_avg_s = float(np.mean(topk_ms)) * 1e-3
 
@@ -215,13 +244,14 @@ def main():
         "scaling": "weak",
         "vs_baseline": (round(value / (256 * 32770 / (PAGES_SELECT_MS * 1e-3)), 3)
                         if w.name == synth.HEADLINE else None),
-        "dtype": "f32",
+        "dtype": "bf16x3" if path == "bf16x3" else "f32",
         "data": "synthetic (seeded N(0,1) fp32 queries and block summaries, planted needles)",
         "config": {
             "workload": (f"{w.name}: {w.nq} queries x {w.active} active blocks "
                          f"({w.capacity}-block capacity), {w.heads} heads x {w.dim}, k={w.k}"),
             "nq": w.nq, "active_blocks": w.active, "capacity_blocks": w.capacity,
             "heads": w.heads, "dim": w.dim, "k": w.k, "input_copies": ncopy,
+            "scores_mode": mode,
         },
         "stages": {
             "scores_ms": round(float(np.mean(score_ms)), 5),
@@ -230,6 +260,8 @@ def main():
             "topk_ms_median": round(float(np.median(topk_ms)), 5),
             "topk_gbs": round(topk_bytes / topk_avg_s / 1e9, 1),
             "topk_hbm_frac": round(topk_bytes / topk_avg_s / 1e9 / PEAK_HBM_GBS, 4),
+            "scores_kernel": path,
+            **extra,
         },
         "roofline": roof,
         "cpu_baseline": None,

@@ -47,6 +47,7 @@ extern "C" {
 #define QSA_ERR_K 3      /* k < 0 or k > QSA_TOPK_MAX_K                             */
 #define QSA_ERR_ALIGN 4  /* q or kblk not 16-byte aligned, scores/ids not 4-byte aligned */
 #define QSA_ERR_LAUNCH 5 /* the HIP runtime rejected a launch (hipGetLastError)     */
+#define QSA_ERR_MODE 6   /* unknown precision mode                                  */
 
 /* Largest heads*dim (elements of one query or one block summary). */
 #define QSA_MAX_HEAD_DIM 4096
@@ -62,13 +63,12 @@ extern "C" {
  *           capacity) are never touched and may hold anything.
  *   scores  out: [nq][active_blocks] fp32, row stride active_blocks.
  *
- * Arithmetic is fp32 in a fixed order that does not depend on a block's
+ * Arithmetic follows a fixed order that does not depend on a block's
  * position, so blocks with identical summaries get bitwise-identical scores
- * within a call.  Small nq (<= 8) uses a bandwidth-bound per-block dot
- * product; larger nq uses fp32 matrix-core (MFMA) tiles with one partial sum
- * per quarter of heads*dim, combined as (p0 + p1) + (p2 + p3).  Either way the
- * error against an exact (FP64) evaluation stays well inside
- * 1e-6 * max|score| for N(0,1) inputs.
+ * within a call.  Small nq (<= 8) uses a bandwidth-bound fp32 per-block dot
+ * product; larger nq uses matrix-core tiles (QSA_SCORES_AUTO of
+ * qsa_block_scores_ex below).  The error against an exact (FP64) evaluation
+ * stays well inside 1e-6 * max|score| for N(0,1) inputs.
  *
  * nq == 0 or active_blocks == 0 is a successful no-op.  Non-finite inputs give
  * non-finite scores.
@@ -95,6 +95,33 @@ int qsa_block_scores(const float *q, const float *kblk, int nq, int heads, int d
  */
 int qsa_block_topk(const float *scores, int nq, int active_blocks, int k, int *ids,
                    void *stream);
+
+/*
+ * qsa_block_scores_ex -- qsa_block_scores with an explicit precision mode.
+ *
+ *   QSA_SCORES_AUTO    the library's choice (what qsa_block_scores does):
+ *                      nq <= 8 -> fp32 per-block dot products (bandwidth-bound);
+ *                      larger nq -> QSA_SCORES_BF16X3.
+ *   QSA_SCORES_FP32    fp32 arithmetic throughout: the dot-product kernel for
+ *                      nq <= 8, fp32 matrix-core (MFMA) tiles otherwise.
+ *   QSA_SCORES_BF16X3  bf16 matrix cores on an exact three-way split of every
+ *                      fp32 operand into bf16 slices hi + mid + lo, summing the
+ *                      six slice products of order <= 2 with the hi*hi products
+ *                      in their own fp32 accumulator (page "#337 hip: gfx12
+ *                      (RDNA4) QSA select - WMMA block scorer, prompt-aware top-k
+ *                      dispatch", What item 2).  The dropped products are below
+ *                      2^-24 of each term, so the error against FP64 is of the
+ *                      same order as fp32 arithmetic's.
+ *
+ * Every mode keeps each score's arithmetic independent of the block's
+ * position.  Other arguments, layouts and errors as qsa_block_scores; an
+ * unknown mode returns QSA_ERR_MODE.
+ */
+#define QSA_SCORES_AUTO 0
+#define QSA_SCORES_FP32 1
+#define QSA_SCORES_BF16X3 2
+int qsa_block_scores_ex(const float *q, const float *kblk, int nq, int heads, int dim,
+                        int active_blocks, float *scores, int mode, void *stream);
 
 /* Human-readable text of a status code (a static string; never NULL). */
 const char *qsa_strerror(int status);

@@ -18,13 +18,17 @@ _LIB_NAME = "libqsa.so"
 
 # Mirrors of include/qsa.h.
 QSA_OK, QSA_ERR_NULL, QSA_ERR_SHAPE, QSA_ERR_K, QSA_ERR_ALIGN, QSA_ERR_LAUNCH = 0, 1, 2, 3, 4, 5
+QSA_ERR_MODE = 6
 QSA_MAX_HEAD_DIM = 4096
 TOPK_MAX_K = 4096
+QSA_SCORES_AUTO, QSA_SCORES_FP32, QSA_SCORES_BF16X3 = 0, 1, 2
+SCORE_MODES = {"auto": QSA_SCORES_AUTO, "fp32": QSA_SCORES_FP32, "bf16x3": QSA_SCORES_BF16X3}
 
 # Entry points declared in include/qsa.h: name -> (restype, argtypes).
 _VP, _I = ctypes.c_void_p, ctypes.c_int
 SIGNATURES = {
     "qsa_block_scores": (_I, [_VP, _VP, _I, _I, _I, _I, _VP, _VP]),
+    "qsa_block_scores_ex": (_I, [_VP, _VP, _I, _I, _I, _I, _VP, _I, _VP]),
     "qsa_block_topk": (_I, [_VP, _I, _I, _I, _VP, _VP]),
     "qsa_strerror": (ctypes.c_char_p, [_I]),
 }
@@ -76,11 +80,12 @@ def _require_gpu_f32(name: str, t: torch.Tensor, ndim: int):
         raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
 
 
-def qsa_block_scores(q: torch.Tensor, kblk: torch.Tensor, active_blocks: int | None = None,
-                     scores: torch.Tensor | None = None) -> torch.Tensor:
+def qsa_block_scores_ex(q: torch.Tensor, kblk: torch.Tensor, active_blocks: int | None = None,
+                        scores: torch.Tensor | None = None, mode="auto") -> torch.Tensor:
     """Scores [nq, active_blocks] of q [nq, heads, dim] against kblk [C, heads, dim].
 
     Only rows [0, active_blocks) of kblk are read (default: all C rows).
+    mode: "auto" | "fp32" | "bf16x3" (or the QSA_SCORES_* integer).
     """
     _require_gpu_f32("q", q, 3)
     _require_gpu_f32("kblk", kblk, 3)
@@ -90,6 +95,7 @@ def qsa_block_scores(q: torch.Tensor, kblk: torch.Tensor, active_blocks: int | N
     a = kblk.shape[0] if active_blocks is None else int(active_blocks)
     if not 0 <= a <= kblk.shape[0]:
         raise ValueError(f"active_blocks={a} outside [0, {kblk.shape[0]}]")
+    m = SCORE_MODES[mode] if isinstance(mode, str) else int(mode)
     if scores is None:
         scores = torch.empty((nq, a), dtype=torch.float32, device=q.device)
     else:
@@ -97,11 +103,17 @@ def qsa_block_scores(q: torch.Tensor, kblk: torch.Tensor, active_blocks: int | N
         if tuple(scores.shape) != (nq, a) or scores.device != q.device:
             raise ValueError(f"scores must be [{nq}, {a}] on q's device")
     with torch.cuda.device(q.device):
-        st = load_library().qsa_block_scores(q.data_ptr(), kblk.data_ptr(), nq, heads, dim, a,
-                                             scores.data_ptr(), _stream_handle(q.device))
+        st = load_library().qsa_block_scores_ex(q.data_ptr(), kblk.data_ptr(), nq, heads, dim, a,
+                                                scores.data_ptr(), m, _stream_handle(q.device))
     if st != QSA_OK:
-        raise QSAError(st, "qsa_block_scores")
+        raise QSAError(st, "qsa_block_scores_ex")
     return scores
+
+
+def qsa_block_scores(q: torch.Tensor, kblk: torch.Tensor, active_blocks: int | None = None,
+                     scores: torch.Tensor | None = None) -> torch.Tensor:
+    """Scores [nq, active_blocks] with the library's default precision mode."""
+    return qsa_block_scores_ex(q, kblk, active_blocks, scores, QSA_SCORES_AUTO)
 
 
 def qsa_block_topk(scores: torch.Tensor, k: int, ids: torch.Tensor | None = None) -> torch.Tensor:

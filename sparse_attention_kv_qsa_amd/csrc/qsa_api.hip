@@ -9,6 +9,9 @@
 #include "qsa_internal.h"
 
 static_assert(QSA_TOPK_MAX_K == qsa::kTopkMaxK, "header and kernels disagree on the top-k limit");
+static_assert(QSA_SCORES_AUTO == qsa::kScoresAuto && QSA_SCORES_FP32 == qsa::kScoresFp32 &&
+                  QSA_SCORES_BF16X3 == qsa::kScoresBf16x3,
+              "header and kernels disagree on the precision modes");
 
 namespace {
 
@@ -18,17 +21,25 @@ int launch_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_LAUN
 
 }  // namespace
 
-extern "C" int qsa_block_scores(const float *q, const float *kblk, int nq, int heads, int dim,
-                                int active_blocks, float *scores, void *stream) {
+extern "C" int qsa_block_scores_ex(const float *q, const float *kblk, int nq, int heads, int dim,
+                                   int active_blocks, float *scores, int mode, void *stream) {
   if (nq < 0 || heads < 0 || dim < 0 || active_blocks < 0) return QSA_ERR_SHAPE;
   const int64_t K = int64_t(heads) * dim;
   if (K < 4 || K % 4 != 0 || K > QSA_MAX_HEAD_DIM) return QSA_ERR_SHAPE;
+  if (mode != QSA_SCORES_AUTO && mode != QSA_SCORES_FP32 && mode != QSA_SCORES_BF16X3)
+    return QSA_ERR_MODE;
   if (nq == 0 || active_blocks == 0) return QSA_OK;
   if (!q || !kblk || !scores) return QSA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(kblk, 16) || !aligned(scores, 4)) return QSA_ERR_ALIGN;
   (void)hipGetLastError();  // start from a clean launch status
-  return launch_status(qsa::launch_block_scores(q, kblk, nq, int(K), active_blocks, scores,
+  return launch_status(qsa::launch_block_scores(q, kblk, nq, int(K), active_blocks, scores, mode,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int qsa_block_scores(const float *q, const float *kblk, int nq, int heads, int dim,
+                                int active_blocks, float *scores, void *stream) {
+  return qsa_block_scores_ex(q, kblk, nq, heads, dim, active_blocks, scores, QSA_SCORES_AUTO,
+                             stream);
 }
 
 extern "C" int qsa_block_topk(const float *scores, int nq, int active_blocks, int k, int *ids,
@@ -57,6 +68,8 @@ extern "C" const char *qsa_strerror(int status) {
       return "misaligned pointer: q/kblk need 16 bytes, scores/ids 4 bytes";
     case QSA_ERR_LAUNCH:
       return "the HIP runtime rejected a kernel launch";
+    case QSA_ERR_MODE:
+      return "unknown precision mode";
     default:
       return "unknown status";
   }

@@ -13,12 +13,25 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkMaxK = 4096;
 // Queries at or below this count take the per-block dot-product scorer.
 constexpr int kGemvMaxQueries = 8;
+// Precision modes (the QSA_SCORES_* values of qsa.h).
+constexpr int kScoresAuto = 0;
+constexpr int kScoresFp32 = 1;
+constexpr int kScoresBf16x3 = 2;
 
 // Scores of nq queries against active_blocks summaries, K = heads*dim fp32
-// elements each.  Chooses the bandwidth-bound dot-product kernel for small nq
-// and the MFMA tile kernel otherwise.
+// elements each, with the given precision mode (QSA_SCORES_* of qsa.h).
 hipError_t launch_block_scores(const float *q, const float *kblk, int nq, int K,
-                               int active_blocks, float *scores, hipStream_t stream);
+                               int active_blocks, float *scores, int mode, hipStream_t stream);
+
+// The same scores on bf16 matrix cores with the exact three-way split of each
+// fp32 operand (six slice products; any nq).
+hipError_t launch_block_scores_bf16x3(const float *q, const float *kblk, int nq, int K,
+                                      int active_blocks, float *scores, hipStream_t stream);
+
+// fp32 scores: the dot-product kernel for nq <= kGemvMaxQueries (and K that
+// fits its registers), else fp32 MFMA tiles.
+hipError_t launch_block_scores_fp32(const float *q, const float *kblk, int nq, int K,
+                                    int active_blocks, float *scores, hipStream_t stream);
 
 // Top-k ids per row of scores[nq][active_blocks]; k in [1, kTopkMaxK].
 hipError_t launch_block_topk(const float *scores, int nq, int active_blocks, int k,

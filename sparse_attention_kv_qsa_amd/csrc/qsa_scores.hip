@@ -321,8 +321,8 @@ bool gemv_fits(int nq, int K) {
 
 }  // namespace
 
-hipError_t launch_block_scores(const float *q, const float *kblk, int nq, int K, int A,
-                               float *scores, hipStream_t stream) {
+hipError_t launch_block_scores_fp32(const float *q, const float *kblk, int nq, int K, int A,
+                                    float *scores, hipStream_t stream) {
   if (gemv_fits(nq, K)) {
     if (nq <= 1) return launch_gemv_nc<1>(q, kblk, nq, K, A, scores, stream);
     if (nq <= 2) return launch_gemv_nc<2>(q, kblk, nq, K, A, scores, stream);
@@ -340,6 +340,17 @@ hipError_t launch_block_scores(const float *q, const float *kblk, int nq, int K,
   }
   scores_mfma_kernel<<<int(8 * per), 256, 0, stream>>>(q, kblk, nq, K, A, scores, nqt, nct, ntail);
   return hipGetLastError();
+}
+
+// Mode dispatch (modes of include/qsa.h).  AUTO: few queries are bandwidth-
+// bound and take the fp32 dot-product kernel; larger batches take the bf16x3
+// split MFMA tiles, whose error against FP64 is of the same order as the fp32
+// MFMA path's at 2.7x its throughput.
+hipError_t launch_block_scores(const float *q, const float *kblk, int nq, int K, int A,
+                               float *scores, int mode, hipStream_t stream) {
+  if (mode == kScoresBf16x3 || (mode == kScoresAuto && !gemv_fits(nq, K)))
+    return launch_block_scores_bf16x3(q, kblk, nq, K, A, scores, stream);
+  return launch_block_scores_fp32(q, kblk, nq, K, A, scores, stream);
 }
 
 }  // namespace qsa

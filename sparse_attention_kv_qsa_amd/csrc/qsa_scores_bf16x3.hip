@@ -1,0 +1,273 @@
+// Block scoring on bf16 matrix cores with an exact three-way split (gfx950).
+//
+// Page "#337 hip: gfx12 (RDNA4) QSA select - WMMA block scorer, prompt-aware
+// top-k dispatch", What item 2: every fp32 operand x is cut into three bf16
+// numbers hi + mid + lo == x exactly (each holds the next 8 significant bits:
+// hi is x truncated to bf16, mid is (x - hi) truncated, lo = x - hi - mid),
+// and a product q*k is formed from the six slice products of order <= 2:
+//   hi*hi  +  [hi*mid + mid*hi + hi*lo + mid*mid + lo*hi],
+// dropping mid*lo, lo*mid and lo*lo (each below 2^-24 of |q*k|).  Every slice
+// product is exact in fp32.  The hi*hi products get their own accumulator and
+// the five corrections another, added once at the end, so the corrections are
+// not rounded at the large accumulator's ulp.
+//
+// On CDNA4 the dense bf16 matrix rate is 16x the fp32 one, so six bf16 MFMAs
+// per fp32-equivalent product still run ~2.7x faster than fp32 MFMA.
+//
+// Workgroup tile: 128 queries x 64 blocks, 4 waves.  Wave w owns queries
+// [32w, 32w + 32) against both 32-block halves of the tile over the whole of
+// K, in steps of 32 = two 16-element halves (v_mfma_f32_32x32x16_bf16; lane l
+// supplies row l%32, K elements 8*(l/32) .. +7 of a half, and holds rows
+// 8*(r/4) + 4*(l/32) + r%4 of column l%32 of the result in register r).  The
+// block summaries of a step are shared by the four waves: thread t loads 8
+// consecutive elements of block row t/4, splits them and writes the three
+// 16-byte planes to LDS exactly where the MFMA lane that needs them will read
+// them; two LDS buffers alternate, one barrier per step.  Each wave splits its
+// own query slices in registers.  A wave keeps eight accumulators per tile
+// column half: hi*hi and corrections, each separately for the two K halves
+// of a step (so that no accumulator is reused within four MFMAs); the score
+// is (hh_0 + hh_1) + (c_0 + c_1).  No cross-wave combine: each wave stores
+// its 32 x 64 results from registers.
+//
+// Position invariance: a ragged tile runs the same per-element instruction
+// sequence (hardware-bounded buffer loads return zeros past the valid rows;
+// zero slices add exact zeros), so equal summaries score bitwise-equal.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 128;  // queries per tile
+constexpr int BN = 64;   // blocks per tile
+constexpr int BK = 32;   // K elements per step
+constexpr uint32_t kOutOfRange = 0x40000000u;  // byte offset past any tile resource
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const float *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, int(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ f4 buffer_f4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// The three bf16 planes of 8 consecutive fp32 values (x[0..3] = a, x[4..7] = b),
+// each packed as 8 bf16 (element 2i in the low half of word i).
+struct Planes {
+  u4 hi, mid, lo;
+};
+
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t even, uint32_t odd) {
+  // low half <- even[31:16], high half <- odd[31:16]
+  return __builtin_amdgcn_perm(odd, even, 0x07060302u);
+}
+
+__device__ __forceinline__ Planes split8(f4 a, f4 b) {
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t hb[8], mb[8], lb[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t u = __float_as_uint(x[i]);
+    hb[i] = u;                                          // hi = top 16 bits of u
+    const float r1 = x[i] - __uint_as_float(u & 0xFFFF0000u);  // exact: <= 16 significant bits
+    const uint32_t v = __float_as_uint(r1);
+    mb[i] = v;                                          // mid = top 16 bits of r1
+    const float r2 = r1 - __uint_as_float(v & 0xFFFF0000u);    // exact: <= 8 significant bits
+    lb[i] = __float_as_uint(r2);                        // lo = r2, exact in bf16
+  }
+  Planes p;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    p.hi[w] = pack_hi16(hb[2 * w], hb[2 * w + 1]);
+    p.mid[w] = pack_hi16(mb[2 * w], mb[2 * w + 1]);
+    p.lo[w] = pack_hi16(lb[2 * w], lb[2 * w + 1]);
+  }
+  return p;
+}
+
+__device__ __forceinline__ f16v mfma_bf16(u4 a, u4 b, f16v c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8, a),
+                                                 __builtin_bit_cast(bf8, b), c, 0, 0, 0);
+}
+
+// One 128 x 64 tile.  FULL: all 64 block rows active; otherwise a 32-block
+// half without an active block skips its MFMAs.
+template <bool FULL>
+__device__ __forceinline__ void split_tile(const float *__restrict__ q,
+                                           const float *__restrict__ kblk, int nq, int K, int A,
+                                           float *__restrict__ scores, int q0, int b0, u4 *bl) {
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int r32 = lane & 31;
+  const int h = lane >> 5;
+  const int nni = FULL ? 2 : min(2, (A - b0 + 31) / 32);
+
+  const uint32_t row_bytes = uint32_t(K) * 4u;
+  const __amdgpu_buffer_rsrc_t rq = tile_rsrc(q + int64_t(q0) * K, uint32_t(min(BM, nq - q0)) * row_bytes);
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kblk + int64_t(b0) * K, uint32_t(min(BN, A - b0)) * row_bytes);
+
+  // Query slices: lane supplies row 32*wave + r32, elements kk + 16*ks + 8h .. +7.
+  const uint32_t qrow = uint32_t(32 * wave + r32) * row_bytes;
+  // Block share: thread t loads row t/4, elements kk + 8*(t%4) .. +7, i.e. K
+  // half ks = (t%4)/2 of MFMA lane (row%32) + 32*((t%4)%2) of column half row/32.
+  const int brow = t >> 2;
+  const int bkg = t & 3;
+  const uint32_t boff = uint32_t(brow) * row_bytes;
+  const int bslot = ((bkg >> 1) * 2 + (brow >> 5)) * 64 + (brow & 31) + 32 * (bkg & 1);
+  constexpr int kPlane = 2 * 2 * 64;  // u4 entries per plane of one step
+
+  auto eoff = [&](int e) -> uint32_t { return e < K ? uint32_t(e) * 4u : kOutOfRange; };
+
+  // acc[ks][set][ni]: set 0 = hi*hi, set 1 = corrections; ks = K half of a step.
+  f16v acc[2][2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) acc[a][c][ni] = f16v{};
+
+  f4 qa[2][2], kb[2];
+  auto load = [&](int kk) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      qa[ks][0] = buffer_f4(rq, qrow + eoff(kk + 16 * ks + 8 * h));
+      qa[ks][1] = buffer_f4(rq, qrow + eoff(kk + 16 * ks + 8 * h + 4));
+    }
+    kb[0] = buffer_f4(rk, boff + eoff(kk + 8 * bkg));
+    kb[1] = buffer_f4(rk, boff + eoff(kk + 8 * bkg + 4));
+  };
+  auto publish = [&](u4 *buf) {
+    const Planes pb = split8(kb[0], kb[1]);
+    buf[0 * kPlane + bslot] = pb.hi;
+    buf[1 * kPlane + bslot] = pb.mid;
+    buf[2 * kPlane + bslot] = pb.lo;
+  };
+
+  // Software pipeline over 32-element steps.  At the top of step s the wave
+  // splits the raw data of step s + 1 (its query slices into registers, its
+  // share of the block slices into the other LDS buffer) and at once issues
+  // the loads of step s + 2, so they have the whole MFMA section of step s to
+  // arrive; a scheduling barrier keeps the compiler from sinking them.  One
+  // workgroup barrier per step publishes the next buffer and retires the
+  // reads of the buffer it will overwrite.  The loop is unrolled by two so
+  // the query planes of consecutive steps alternate between two register
+  // sets instead of being copied.
+  const int nsteps = (K + BK - 1) / BK;
+  auto step = [&](int s, const Planes (&use)[2], Planes (&fill)[2]) {
+    const u4 *cur = bl + (s & 1) * (3 * kPlane);
+    u4 *nxt = bl + ((s + 1) & 1) * (3 * kPlane);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) fill[ks] = split8(qa[ks][0], qa[ks][1]);
+    publish(nxt);
+    load((s + 2) * BK);  // past K: out-of-range offsets, no memory access
+    __builtin_amdgcn_sched_barrier(0);
+    Planes pbv[2][2];  // [ks][ni]
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        if (FULL || ni < nni) {
+          const int o = (ks * 2 + ni) * 64 + lane;
+          pbv[ks][ni].hi = cur[0 * kPlane + o];
+          pbv[ks][ni].mid = cur[1 * kPlane + o];
+          pbv[ks][ni].lo = cur[2 * kPlane + o];
+        }
+      }
+    // Product order, fixed for every element: hi*hi into the hh set; then
+    // hi*mid, mid*hi, hi*lo, mid*mid, lo*hi into the correction set.
+#pragma unroll
+    for (int p = 0; p < 6; ++p)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          if (!(FULL || ni < nni)) continue;
+          const Planes &x = use[ks];
+          const Planes &y = pbv[ks][ni];
+          switch (p) {
+            case 0: acc[ks][0][ni] = mfma_bf16(x.hi, y.hi, acc[ks][0][ni]); break;
+            case 1: acc[ks][1][ni] = mfma_bf16(x.hi, y.mid, acc[ks][1][ni]); break;
+            case 2: acc[ks][1][ni] = mfma_bf16(x.mid, y.hi, acc[ks][1][ni]); break;
+            case 3: acc[ks][1][ni] = mfma_bf16(x.hi, y.lo, acc[ks][1][ni]); break;
+            case 4: acc[ks][1][ni] = mfma_bf16(x.mid, y.mid, acc[ks][1][ni]); break;
+            default: acc[ks][1][ni] = mfma_bf16(x.lo, y.hi, acc[ks][1][ni]); break;
+          }
+        }
+    __syncthreads();
+  };
+
+  Planes pa[2], pn[2];
+  load(0);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) pa[ks] = split8(qa[ks][0], qa[ks][1]);
+  publish(bl);
+  load(BK);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, pa, pn);
+    if (s + 1 < nsteps) step(s + 1, pn, pa);
+  }
+
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) {
+    const f16v v = (acc[0][0][ni] + acc[1][0][ni]) + (acc[0][1][ni] + acc[1][1][ni]);
+    const int col = b0 + 32 * ni + r32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = q0 + 32 * wave + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row < nq && col < A) scores[int64_t(row) * A + col] = v[r];
+    }
+  }
+}
+
+// Tile assignment as in the fp32 scorer: workgroup ids go round-robin over
+// the 8 XCDs; each XCD takes an equal share of the full tiles (query tiles
+// of one block tile adjacent) and every eighth ragged tile, ragged first.
+__global__ __launch_bounds__(256, 2) void scores_bf16x3_kernel(const float *__restrict__ q,
+                                                               const float *__restrict__ kblk,
+                                                               int nq, int K, int A,
+                                                               float *__restrict__ scores,
+                                                               int nqt, int nct, int ntail) {
+  __shared__ u4 bl[2 * 3 * 2 * 2 * 64];  // 24 KB: two steps x three planes x (2 K halves x 2 column halves x 64 lanes)
+  const int x = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int tails_here = ntail > x ? (ntail - x + 7) / 8 : 0;
+  if (slot < tails_here) {
+    split_tile<false>(q, kblk, nq, K, A, scores, (x + 8 * slot) * BM, (nct - 1) * BN, bl);
+    return;
+  }
+  const int64_t nfull = int64_t(nqt) * (nct - (ntail > 0 ? 1 : 0));
+  const int64_t f = nfull * x / 8 + (slot - tails_here);
+  if (f >= nfull * (x + 1) / 8) return;  // whole workgroup leaves before any barrier
+  split_tile<true>(q, kblk, nq, K, A, scores, int(f % nqt) * BM, int(f / nqt) * BN, bl);
+}
+
+}  // namespace
+
+hipError_t launch_block_scores_bf16x3(const float *q, const float *kblk, int nq, int K, int A,
+                                      float *scores, hipStream_t stream) {
+  const int nqt = (nq + BM - 1) / BM;
+  const int nct = (A + BN - 1) / BN;
+  const int ntail = (A % BN) ? nqt : 0;
+  const int64_t nfull = int64_t(nqt) * (nct - (ntail ? 1 : 0));
+  int64_t per = 0;  // workgroups per XCD: the largest share
+  for (int x = 0; x < 8; ++x) {
+    const int64_t tails = ntail > x ? (ntail - x + 7) / 8 : 0;
+    per = std::max(per, tails + nfull * (x + 1) / 8 - nfull * x / 8);
+  }
+  scores_bf16x3_kernel<<<int(8 * per), 256, 0, stream>>>(q, kblk, nq, K, A, scores, nqt, nct,
+                                                         ntail);
+  return hipGetLastError();
+}
+
+}  // namespace qsa

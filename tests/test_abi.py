@@ -22,7 +22,7 @@ def header_entry_points() -> list[str]:
 
 
 def header_macros() -> dict[str, int]:
-    return {m: int(v) for m, v in re.findall(r"#define\s+(QSA_[A-Z_]+)\s+(\d+)", open(HEADER).read())}
+    return {m: int(v) for m, v in re.findall(r"#define\s+(QSA_[A-Z0-9_]+)\s+(\d+)", open(HEADER).read())}
 
 
 @pytest.fixture(scope="module")
@@ -33,7 +33,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert header_entry_points() == ["qsa_block_scores", "qsa_block_topk", "qsa_strerror"]
+    assert header_entry_points() == ["qsa_block_scores", "qsa_block_scores_ex", "qsa_block_topk",
+                                     "qsa_strerror"]
 
 
 def test_binding_covers_the_header():
@@ -44,6 +45,9 @@ def test_binding_covers_the_header():
         binding.QSA_OK, binding.QSA_ERR_NULL, binding.QSA_ERR_SHAPE, binding.QSA_ERR_K,
         binding.QSA_ERR_ALIGN, binding.QSA_ERR_LAUNCH)
     assert mac["QSA_TOPK_MAX_K"] == binding.TOPK_MAX_K
+    assert mac["QSA_ERR_MODE"] == binding.QSA_ERR_MODE
+    assert (mac["QSA_SCORES_AUTO"], mac["QSA_SCORES_FP32"], mac["QSA_SCORES_BF16X3"]) == (
+        binding.QSA_SCORES_AUTO, binding.QSA_SCORES_FP32, binding.QSA_SCORES_BF16X3)
     assert mac["QSA_MAX_HEAD_DIM"] == binding.QSA_MAX_HEAD_DIM
 
 
@@ -64,7 +68,7 @@ def test_library_is_built_for_gfx950_only():
 
 
 def test_strerror(lib):
-    for code in range(6):
+    for code in range(7):
         assert binding.qsa_strerror(code)
     assert binding.qsa_strerror(0) == "success"
     assert binding.qsa_strerror(99) == "unknown status"
@@ -94,6 +98,12 @@ P4 = 0x10004
 ])
 def test_block_scores_argument_checks(lib, args, status):
     assert lib.qsa_block_scores(*args, None) == status
+
+
+@pytest.mark.parametrize("mode,status", [(0, 0), (1, 0), (2, 0), (3, 6), (-1, 6)])
+def test_block_scores_ex_mode_check(lib, mode, status):
+    # a valid mode on an empty call is a no-op; an unknown mode is rejected first
+    assert lib.qsa_block_scores_ex(None, None, 0, 4, 128, 10, None, mode, None) == status
 
 
 @pytest.mark.parametrize("args,status", [

@@ -38,9 +38,13 @@ def gpu():
     return lib
 
 
-def gpu_scores(q: np.ndarray, kblk: np.ndarray, active: int) -> np.ndarray:
-    from sparse_attention_kv_qsa_amd import qsa_block_scores
-    s = qsa_block_scores(torch.from_numpy(q).cuda(), torch.from_numpy(kblk).cuda(), active)
+MODES = ["fp32", "bf16x3"]  # "auto" is one of these for every shape
+
+
+def gpu_scores(q: np.ndarray, kblk: np.ndarray, active: int, mode="auto") -> np.ndarray:
+    from sparse_attention_kv_qsa_amd import qsa_block_scores_ex
+    s = qsa_block_scores_ex(torch.from_numpy(q).cuda(), torch.from_numpy(kblk).cuda(), active,
+                            mode=mode)
     torch.cuda.synchronize()
     return s.cpu().numpy()
 
@@ -72,13 +76,14 @@ def check_topk(scores, k):
 
 # ------------------------------------------------------------ scores ----
 
-def test_hand_example_bitwise():
+@pytest.mark.parametrize("mode", ["auto"] + MODES)
+def test_hand_example_bitwise(mode):
     from test_oracle import load_hand_example
     q, b, scores, topks = load_hand_example()
     want = np.array([scores[i] for i in sorted(scores)], np.float32)
     for reps in (1, 9):  # nq = 2 takes the dot-product kernel, nq = 18 the MFMA tiles
         qq = np.ascontiguousarray(np.tile(q, (reps, 1, 1)))
-        s = gpu_scores(qq, b, 3)
+        s = gpu_scores(qq, b, 3, mode)
         assert np.array_equal(s, np.tile(want, (reps, 1)))
     for i, k, ids in topks:
         assert gpu_topk(want[i:i + 1], k)[0].tolist() == ids
@@ -91,11 +96,12 @@ INT_CASES = [  # nq, heads, dim, active (ragged tails against 16/64-wide tiles)
 ]
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("nq,heads,dim,active", INT_CASES)
-def test_integer_inputs_bitwise(nq, heads, dim, active):
+def test_integer_inputs_bitwise(nq, heads, dim, active, mode):
     q, kb = synth.make_random(nq, heads, dim, active, capacity=active + 5, seed=nq + active,
                               integer=True)
-    s = gpu_scores(q, kb, active)
+    s = gpu_scores(q, kb, active, mode)
     s64 = ORC.scores_f64(q, kb, active)
     assert np.array_equal(s.astype(np.float64), s64)
 
@@ -108,22 +114,24 @@ RAND_CASES = [  # nq, heads, dim, active
 ]
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("nq,heads,dim,active", RAND_CASES)
-def test_scores_within_gate(nq, heads, dim, active):
+def test_scores_within_gate(nq, heads, dim, active, mode):
     q, kb = synth.make_random(nq, heads, dim, active, capacity=active + 3, seed=7 * nq + dim)
-    s = gpu_scores(q, kb, active)
+    s = gpu_scores(q, kb, active, mode)
     assert np.all(np.isfinite(s)), "poisoned capacity rows were read"
     check_scores(s, ORC.scores_f64(q, kb, active))
 
 
-def test_scores_deterministic_and_position_invariant():
+@pytest.mark.parametrize("mode", MODES)
+def test_scores_deterministic_and_position_invariant(mode):
     rng = np.random.default_rng(12)
-    for nq in (1, 5, 100):
+    for nq in (1, 5, 100, 300):
         vec = rng.standard_normal((4, 4, 128)).astype(np.float32)
         assign = rng.integers(0, 4, 700)
         kb = np.ascontiguousarray(vec[assign])
         q = rng.standard_normal((nq, 4, 128)).astype(np.float32)
-        s1, s2 = gpu_scores(q, kb, 700), gpu_scores(q, kb, 700)
+        s1, s2 = gpu_scores(q, kb, 700, mode), gpu_scores(q, kb, 700, mode)
         assert np.array_equal(s1, s2)
         for c in range(4):
             cols = s1[:, assign == c]
@@ -222,17 +230,18 @@ SAMPLE_ROWS = 6
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("mode", ["auto", "fp32"])
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
-def test_workload_parity(name):
+def test_workload_parity(name, mode):
     w = synth.WORKLOADS[name]
-    print(f"\n[workload {name}] nq={w.nq} A={w.active} C={w.capacity} K={w.K} k={w.k}",
+    print(f"\n[workload {name} {mode}] nq={w.nq} A={w.active} C={w.capacity} K={w.K} k={w.k}",
           flush=True)
     bt = synth.make_batch(w)
-    from sparse_attention_kv_qsa_amd import qsa_block_scores, qsa_block_topk
+    from sparse_attention_kv_qsa_amd import qsa_block_scores_ex, qsa_block_topk
     qt, kt = torch.from_numpy(bt.q).cuda(), torch.from_numpy(bt.kblk).cuda()
-    s_t = qsa_block_scores(qt, kt, w.active)
+    s_t = qsa_block_scores_ex(qt, kt, w.active, mode=mode)
     ids_t = qsa_block_topk(s_t, w.k)
-    s_t2 = qsa_block_scores(qt, kt, w.active)
+    s_t2 = qsa_block_scores_ex(qt, kt, w.active, mode=mode)
     ids_t2 = qsa_block_topk(s_t2, w.k)
     torch.cuda.synchronize()
     s, ids = s_t.cpu().numpy(), ids_t.cpu().numpy()
@@ -243,7 +252,8 @@ def test_workload_parity(name):
     rows = np.unique(np.concatenate([[0, w.nq - 1], rng.integers(0, w.nq, SAMPLE_ROWS)]))
     s64 = ORC.scores_f64(bt.q[rows], bt.kblk, w.active)
     ratio = check_scores(s[rows], s64)
-    print(f"[workload {name}] score error {ratio:.3f}x gate on rows {rows.tolist()}", flush=True)
+    print(f"[workload {name} {mode}] score error {ratio:.3f}x gate on rows {rows.tolist()}",
+          flush=True)
 
     want = ORC.topk(s, w.k)
     assert np.array_equal(ids, want), f"{np.sum(np.any(ids != want, axis=1))} rows differ"
