@@ -19,8 +19,16 @@
  *
  * Conventions for every entry point:
  *   - Every data pointer is a DEVICE pointer on the current HIP device, owned
- *     by the caller.  The library allocates nothing, keeps no global state and
- *     may be called from several host threads at once.
+ *     by the caller.  Some launches also need device scratch (the split
+ *     queries of the bf16x3 scorer, the candidate lists of the few-row
+ *     top-k); the library keeps one scratch buffer per (device, stream),
+ *     allocated with hipMalloc on first need, grown when a call needs more
+ *     and never freed before the process ends.  Work on one stream runs in
+ *     order, so calls on the same stream share it safely; calls on different
+ *     streams use different buffers.  The first call of a given size on a
+ *     stream may therefore allocate: make it before capturing that stream
+ *     into a HIP graph.  The library may be called from several host threads
+ *     at once.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *     void*; NULL = the default stream).  The call returns once the work is
  *     enqueued; results are valid after the stream is synchronised.
@@ -48,11 +56,16 @@ extern "C" {
 #define QSA_ERR_ALIGN 4  /* q or kblk not 16-byte aligned, scores/ids not 4-byte aligned */
 #define QSA_ERR_LAUNCH 5 /* the HIP runtime rejected a launch (hipGetLastError)     */
 #define QSA_ERR_MODE 6   /* unknown precision mode                                  */
+#define QSA_ERR_NOMEM 7  /* the library's device scratch could not be allocated     */
 
 /* Largest heads*dim (elements of one query or one block summary). */
 #define QSA_MAX_HEAD_DIM 4096
 /* Largest k accepted by qsa_block_topk. */
 #define QSA_TOPK_MAX_K 4096
+/* qsa_block_topk spreads each row over the whole GPU when nq is at most this
+ * (decode); larger batches select one row per workgroup.  Either way the
+ * result is the same. */
+#define QSA_TOPK_FEW_ROWS 16
 
 /*
  * qsa_block_scores -- exact block scores (step 1 above).

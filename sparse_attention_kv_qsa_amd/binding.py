@@ -19,8 +19,10 @@ _LIB_NAME = "libqsa.so"
 # Mirrors of include/qsa.h.
 QSA_OK, QSA_ERR_NULL, QSA_ERR_SHAPE, QSA_ERR_K, QSA_ERR_ALIGN, QSA_ERR_LAUNCH = 0, 1, 2, 3, 4, 5
 QSA_ERR_MODE = 6
+QSA_ERR_NOMEM = 7
 QSA_MAX_HEAD_DIM = 4096
 TOPK_MAX_K = 4096
+TOPK_FEW_ROWS = 16
 QSA_SCORES_AUTO, QSA_SCORES_FP32, QSA_SCORES_BF16X3 = 0, 1, 2
 SCORE_MODES = {"auto": QSA_SCORES_AUTO, "fp32": QSA_SCORES_FP32, "bf16x3": QSA_SCORES_BF16X3}
 

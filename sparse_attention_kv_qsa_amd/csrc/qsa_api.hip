@@ -9,6 +9,7 @@
 #include "qsa_internal.h"
 
 static_assert(QSA_TOPK_MAX_K == qsa::kTopkMaxK, "header and kernels disagree on the top-k limit");
+static_assert(QSA_TOPK_FEW_ROWS == qsa::kWideMaxRows, "header and kernels disagree on the few-row path");
 static_assert(QSA_SCORES_AUTO == qsa::kScoresAuto && QSA_SCORES_FP32 == qsa::kScoresFp32 &&
                   QSA_SCORES_BF16X3 == qsa::kScoresBf16x3,
               "header and kernels disagree on the precision modes");
@@ -17,7 +18,10 @@ namespace {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-int launch_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH; }
+int launch_status(hipError_t e) {
+  if (e == hipSuccess) return QSA_OK;
+  return e == hipErrorOutOfMemory ? QSA_ERR_NOMEM : QSA_ERR_LAUNCH;
+}
 
 }  // namespace
 
@@ -70,6 +74,8 @@ extern "C" const char *qsa_strerror(int status) {
       return "the HIP runtime rejected a kernel launch";
     case QSA_ERR_MODE:
       return "unknown precision mode";
+    case QSA_ERR_NOMEM:
+      return "the library could not allocate its device scratch";
     default:
       return "unknown status";
   }

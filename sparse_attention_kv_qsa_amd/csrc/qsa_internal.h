@@ -11,6 +11,9 @@ namespace qsa {
 constexpr int kTopkThreads = 1024;
 // Largest k the top-k kernels sort in LDS.
 constexpr int kTopkMaxK = 4096;
+// Rows at or below this count take the whole-GPU top-k (two launches, the
+// row spread over many workgroups) instead of one workgroup per row.
+constexpr int kWideMaxRows = 16;
 // Queries at or below this count take the per-block dot-product scorer.
 constexpr int kGemvMaxQueries = 8;
 // Precision modes (the QSA_SCORES_* values of qsa.h).
@@ -32,6 +35,11 @@ hipError_t launch_block_scores_bf16x3(const float *q, const float *kblk, int nq,
 // fits its registers), else fp32 MFMA tiles.
 hipError_t launch_block_scores_fp32(const float *q, const float *kblk, int nq, int K,
                                     int active_blocks, float *scores, hipStream_t stream);
+
+// Device scratch of at least `bytes` bytes for work enqueued on `stream` of
+// the current device (qsa_workspace.hip): one growing buffer per (device,
+// stream), so consecutive calls on one stream reuse it in stream order.
+hipError_t workspace(hipStream_t stream, size_t bytes, void **ptr);
 
 // Top-k ids per row of scores[nq][active_blocks]; k in [1, kTopkMaxK].
 hipError_t launch_block_topk(const float *scores, int nq, int active_blocks, int k,

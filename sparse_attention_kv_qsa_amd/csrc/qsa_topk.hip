@@ -117,6 +117,25 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP lane shifts:
+// four shifts within each row of 16 lanes, then the row totals carried
+// forward with row broadcasts (lane 15 -> row 1 and 3, lane 31 -> rows 2, 3).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  int x = int(v);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return uint32_t(x);
+}
+
+// Sum over the wave, the same in every lane.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
+}
+
 // Given the histogram of the current digit in sh.hsub (complete: the caller
 // has passed a barrier), find the digit d* holding the kr-th largest
 // candidate.  Returns d*, the rank left inside that bin and the bin's size.
@@ -138,12 +157,7 @@ __device__ __forceinline__ void find_digit(TopkShared &sh, uint32_t sub0, uint32
       sh.hsub[w][d] = 0;
     }
     if (d == 0) h -= sub0;
-    v = h;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t y = __shfl_up(v, off, 64);
-      if (lane >= off) v += y;
-    }
+    v = wave_incl_scan(h);
     if (lane == 63) sh.wtot[wave] = v;
   }
   __syncthreads();
@@ -341,15 +355,14 @@ struct RowKeys {
   uint32_t key[PER > 0 ? PER : 1];
 };
 
+// Selects one row with the whole workgroup (NT threads): srow[0, A) -> the
+// k ids of orow.  Every thread of the workgroup must call it.
 template <int PER>
-__global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scores, int A, int k,
-                                                  int *__restrict__ ids) {
-  __shared__ TopkShared sh;
+__device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, int k,
+                                         int *__restrict__ orow, TopkShared &sh) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  const float *srow = scores + int64_t(blockIdx.x) * A;
-  int *orow = ids + int64_t(blockIdx.x) * k;
   const int m = min(k, A);
 
   if (m == 0) {  // no active blocks: every slot is padding
@@ -484,6 +497,358 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
 }
 
 template <int PER>
+__global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scores, int A, int k,
+                                                  int *__restrict__ ids) {
+  __shared__ TopkShared sh;
+  topk_row<PER>(scores + int64_t(blockIdx.x) * A, A, k, ids + int64_t(blockIdx.x) * k, sh);
+}
+
+// ---------------------------------------------------------------------------
+// Few-row top-k across the whole GPU.
+//
+// One row of tens of thousands of scores on one workgroup leaves 255 of 256
+// CUs idle and takes a chain of barriers.  With few rows (decode), the row is
+// instead cut into groups of GS = 64 E scores (one wave each) and selected in
+// two launches, with no cross-workgroup synchronisation inside a launch:
+//
+//   1. group_tops_kernel: every group publishes its M best elements, exactly,
+//      as rank words rw = key << 32 | ~id (a larger word ranks first; 0 is an
+//      empty slot).
+//   2. wide_rank_kernel (NB workgroups per row, each doing the same first
+//      steps):
+//      a. a bound: the k-th largest key among the published words lies in
+//         some 4096-bin (top 12 bits) histogram bin; B = that bin's lower
+//         edge.  At least k published elements -- distinct row elements --
+//         have key >= B, so every element of the row's top k has key >= B.
+//      b. the candidates, all elements with key >= B: a group whose M-th
+//         published word is below B ("complete") has all of them among its
+//         published words; the few other groups ("rich") are re-read from
+//         the scores.
+//      c. exact ranks: a candidate's rank is the number of candidates whose
+//         rank word is larger (every element that outranks a candidate is a
+//         candidate).  The candidate list is built in the same order by
+//         every workgroup (prefix sums, no atomics); workgroup j ranks the
+//         j-th of NB slices of it and writes id to ids[rank] when rank < k.
+//   If the candidates overflow LDS (mass ties at the bound), workgroup 0 of
+//   the row runs the one-workgroup selection on the row instead; the result
+//   is the same.
+// ---------------------------------------------------------------------------
+constexpr int WIDE_NB = 16;      // rank workgroups per row (a power of two)
+constexpr int WIDE_CCAP = 4096;  // LDS candidate capacity
+constexpr int WIDE_UCAP = 8192;  // published words per row, at most
+constexpr int WIDE_RCAP = 1024;  // rich groups listed (more: the one-workgroup fallback)
+
+__device__ __forceinline__ uint64_t rank_word(uint32_t key, uint32_t id) {
+  return (uint64_t(key) << 32) | uint64_t(~id);
+}
+
+// Wave maximum of a rank word held as (key, ~id) halves, using lane_xor
+// (DPP within rows of 16 lanes).
+__device__ __forceinline__ uint64_t wave_max_word(uint64_t v) {
+  uint32_t k = uint32_t(v >> 32), i = uint32_t(v);
+  auto step = [&](uint32_t pk, uint32_t pi) {
+    const bool take = (pk > k) | ((pk == k) & (pi > i));
+    k = take ? pk : k;
+    i = take ? pi : i;
+  };
+  step(lane_xor<1>(k), lane_xor<1>(i));
+  step(lane_xor<2>(k), lane_xor<2>(i));
+  step(lane_xor<4>(k), lane_xor<4>(i));
+  step(lane_xor<8>(k), lane_xor<8>(i));
+  step(lane_xor<16>(k), lane_xor<16>(i));
+  step(lane_xor<32>(k), lane_xor<32>(i));
+  return (uint64_t(k) << 32) | i;
+}
+
+// Group g of row blockIdx.y holds ids [g*GS, g*GS + GS); lane l owns ids
+// g*GS + l + 64i (i < E): each load instruction reads 256 contiguous bytes,
+// and ids past the row end read as empty (a hardware-bounded buffer load of
+// a dword past the row returns 0, and the id test discards it).  With E = 1
+// the wave sorts its 64 elements in rank order (a bitonic network on lane
+// exchanges) and lanes 0 .. M-1 hold the group's best; with E > 1 it takes
+// the maximum M times, removing each winner.
+template <int E>
+__global__ __launch_bounds__(256) void group_tops_kernel(const float *__restrict__ scores, int A,
+                                                         int ngroups, int M,
+                                                         uint64_t *__restrict__ tops) {
+  constexpr int GS = 64 * E;
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (g >= ngroups) return;  // wave-uniform; no barriers in this kernel
+  const int row = blockIdx.y;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(scores + int64_t(row) * A), 0, A * 4, 0x00020000);
+  uint32_t raw[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i)
+    raw[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, uint32_t(g * GS + lane + 64 * i) * 4u, 0, 0);
+  uint64_t *dst = tops + (int64_t(row) * ngroups + g) * M;
+  if constexpr (E == 1) {
+    const uint32_t id = uint32_t(g * GS + lane);
+    uint32_t key = id < uint32_t(A) ? score_key(raw[0]) : 0u;
+    uint32_t nid = ~id;  // larger ~id = lower id = earlier in rank order
+    auto first = [](uint32_t ka, uint32_t ia, uint32_t kb, uint32_t ib) {
+      return (ka > kb) | ((ka == kb) & (ia > ib));
+    };
+    bitonic_lane_stage<2, 1>(key, nid, lane, first);
+    bitonic_lane_stage<4, 2>(key, nid, lane, first);
+    bitonic_lane_stage<8, 4>(key, nid, lane, first);
+    bitonic_lane_stage<16, 8>(key, nid, lane, first);
+    bitonic_lane_stage<32, 16>(key, nid, lane, first);
+    bitonic_lane_stage<64, 32>(key, nid, lane, first);
+    if (lane < M) dst[lane] = key ? (uint64_t(key) << 32) | nid : 0ull;
+  } else {
+    uint64_t v[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const uint32_t id = uint32_t(g * GS + lane + 64 * i);
+      v[i] = id < uint32_t(A) ? rank_word(score_key(raw[i]), id) : 0ull;
+    }
+    uint64_t mine = 0;
+    for (int m = 0; m < M; ++m) {
+      uint64_t best = v[0];
+#pragma unroll
+      for (int i = 1; i < E; ++i) best = v[i] > best ? v[i] : best;
+      best = wave_max_word(best);
+      if (best == 0) break;  // the group is exhausted; the rest stay empty
+      if (lane == m) mine = best;
+#pragma unroll
+      for (int i = 0; i < E; ++i) v[i] = v[i] == best ? 0ull : v[i];  // ids are distinct
+    }
+    if (lane < M) dst[lane] = mine;
+  }
+}
+
+struct WideShared {
+  uint32_t hist[4096];
+  uint64_t words[WIDE_UCAP];  // the row's published words
+  uint64_t cand[WIDE_CCAP];
+  uint32_t rich[WIDE_RCAP];
+  uint32_t wsum[NWAVES];
+  uint32_t nvalid, bound;
+};
+
+union WideLds {
+  WideShared w;
+  TopkShared row;
+};
+
+// Exclusive prefix sum of v over the workgroup (NT threads) and the total.
+// One barrier; `wsum` is NWAVES words of scratch.  Every thread must call it.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wsum, uint32_t &total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  const uint32_t ws = wave_incl_scan(lane < NWAVES ? wsum[lane] : 0u);
+  total = __builtin_amdgcn_readlane(ws, NWAVES - 1);
+  const uint32_t before = wave > 0 ? __builtin_amdgcn_readlane(ws, wave - 1) : 0u;
+  return before + incl - v;
+}
+
+template <int E>
+__global__ __launch_bounds__(NT) void wide_rank_kernel(const float *__restrict__ scores, int A,
+                                                       int k, int *__restrict__ ids,
+                                                       const uint64_t *__restrict__ tops,
+                                                       int ngroups, int M) {
+  constexpr int GS = 64 * E;
+  __shared__ WideLds lds;
+  WideShared &sh = lds.w;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int row = blockIdx.y;
+  const float *srow = scores + int64_t(row) * A;
+  int *orow = ids + int64_t(row) * k;
+  const uint64_t *trow = tops + int64_t(row) * ngroups * M;
+  const int U = ngroups * M;  // <= WIDE_UCAP (the launcher sizes M)
+  const int m = min(k, A);
+
+  for (int i = t; i < 4096; i += NT) sh.hist[i] = 0;
+  if (t == 0) sh.nvalid = 0;
+  // The published words, read once (their loads all in flight) and kept in
+  // LDS.
+  constexpr int WPT = WIDE_UCAP / NT;
+  uint64_t wv[WPT];
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int e = t + i * NT;
+    wv[i] = e < U ? trow[e] : 0ull;
+  }
+  __syncthreads();
+
+  // (a) the bound: histogram of the published keys' top 12 bits, then the
+  // bin where the count from the top reaches k.
+  uint32_t nv = 0;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int e = t + i * NT;
+    if (e >= U) break;
+    sh.words[e] = wv[i];
+    const uint32_t key = uint32_t(wv[i] >> 32);
+    if (key) {
+      atomicAdd(&sh.hist[key >> 20], 1u);
+      ++nv;
+    }
+  }
+  nv = wave_sum(nv);
+  if (lane == 0 && nv) atomicAdd(&sh.nvalid, nv);
+  __syncthreads();
+  // Thread t owns bins [4096 - 4(t+1), 4096 - 4t); an exclusive prefix over
+  // threads counts the published keys in higher bins.
+  uint32_t c4 = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c4 += sh.hist[4095 - 4 * t - i];
+  if (t == 0) sh.bound = 1u;  // fewer than k published keys: every real key qualifies
+  uint32_t nvalid_total;
+  uint32_t run = block_excl_scan(c4, sh.wsum, nvalid_total);
+  if (sh.nvalid >= uint32_t(k)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4095 - 4 * t - i;
+      const uint32_t hb = sh.hist[b];
+      if (run < uint32_t(k) && run + hb >= uint32_t(k)) sh.bound = uint32_t(b) << 20;
+      run += hb;
+    }
+  }
+  __syncthreads();
+  const uint32_t B = max(sh.bound, 1u);
+
+  // (b) candidates, in an order every workgroup of the row agrees on: the
+  // published words >= B of complete groups (thread order, then slot
+  // order), then the elements >= B of the rich groups.
+  const int lgM = __builtin_ctz(uint32_t(M));  // M is a power of two
+  bool take[WPT], rich[WPT];
+  uint32_t ntake = 0, nrich = 0;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int e = t + i * NT;
+    take[i] = rich[i] = false;
+    if (e < U) {
+      const int g = e >> lgM;
+      const uint32_t last = uint32_t(sh.words[(g << lgM) + (M - 1)] >> 32);
+      const bool complete = last < B;
+      take[i] = complete && uint32_t(wv[i] >> 32) >= B;
+      rich[i] = !complete && (e == (g << lgM));
+    }
+    ntake += take[i];
+    nrich += rich[i];
+  }
+  uint32_t total;
+  const uint32_t off = block_excl_scan(ntake | (nrich << 16), sh.wsum, total);
+  const uint32_t C0 = total & 0xFFFFu, nr = total >> 16;
+  uint32_t oc = off & 0xFFFFu, orr = off >> 16;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    if (take[i]) {
+      if (oc < uint32_t(WIDE_CCAP)) sh.cand[oc] = wv[i];
+      ++oc;
+    }
+    if (rich[i]) {
+      if (orr < uint32_t(WIDE_RCAP)) sh.rich[orr] = uint32_t((t + i * NT) >> lgM);
+      ++orr;
+    }
+  }
+  uint32_t C = C0;
+  if (nr > 0 && nr <= uint32_t(WIDE_RCAP) && C0 <= uint32_t(WIDE_CCAP)) {
+    __syncthreads();
+    // every element of the rich groups, thread t taking t, t + NT, ...
+    const uint32_t nel = nr * GS;
+    constexpr int RPT = 8;  // elements per thread per pass
+    for (uint32_t base = 0; base < nel; base += RPT * NT) {
+      uint64_t x[RPT];
+      uint32_t c = 0;
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+        const uint32_t i = base + uint32_t(t) + uint32_t(r) * NT;
+        x[r] = 0;
+        if (i < nel) {
+          const uint32_t id = sh.rich[i / GS] * GS + (i % GS);
+          if (id < uint32_t(A)) {
+            const uint32_t key = score_key(__float_as_uint(srow[id]));
+            if (key >= B) x[r] = rank_word(key, id);
+          }
+        }
+        c += x[r] != 0;
+      }
+      uint32_t added;
+      uint32_t o = C + block_excl_scan(c, sh.wsum, added);
+#pragma unroll
+      for (int r = 0; r < RPT; ++r)
+        if (x[r] != 0) {
+          if (o < uint32_t(WIDE_CCAP)) sh.cand[o] = x[r];
+          ++o;
+        }
+      C += added;
+      __syncthreads();  // wsum is reused by the next pass
+    }
+  }
+  __syncthreads();
+
+  if (C > uint32_t(WIDE_CCAP) || nr > uint32_t(WIDE_RCAP)) {
+    // Mass ties at the bound: one workgroup selects the row exactly.
+    if (blockIdx.x == 0) topk_row<-1>(srow, A, k, orow, lds.row);
+    return;
+  }
+
+  // (c) exact ranks of candidates [C*j/NB, C*(j+1)/NB) for workgroup j.  A
+  // wave takes four at a time; its lanes read the list 64 words at a time
+  // and compare each word with all four.
+  const uint32_t c_lo = C * blockIdx.x / gridDim.x, c_hi = C * (blockIdx.x + 1) / gridDim.x;
+  const int wave = t >> 6;
+  for (uint32_t i0 = c_lo + 4u * uint32_t(wave); i0 < c_hi; i0 += 4u * NWAVES) {
+    uint64_t wc[4];
+    uint32_t n[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      wc[c] = i0 + c < c_hi ? sh.cand[i0 + c] : ~0ull;
+      n[c] = 0;
+    }
+    uint32_t j = uint32_t(lane);
+    for (; j + 192 < C; j += 256) {
+      const uint64_t a0 = sh.cand[j], a1 = sh.cand[j + 64], a2 = sh.cand[j + 128],
+                     a3 = sh.cand[j + 192];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        n[c] += (a0 > wc[c] ? 1u : 0u) + (a1 > wc[c] ? 1u : 0u) + (a2 > wc[c] ? 1u : 0u) +
+                (a3 > wc[c] ? 1u : 0u);
+    }
+    for (; j < C; j += 64) {
+      const uint64_t a = sh.cand[j];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) n[c] += a > wc[c] ? 1u : 0u;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t r = wave_sum(n[c]);
+      if (lane == 0 && i0 + c < c_hi && r < uint32_t(k)) orow[r] = int(~uint32_t(wc[c]));
+    }
+  }
+  if (blockIdx.x == 0)
+    for (int r = m + t; r < k; r += NT) orow[r] = -1;
+}
+
+template <int E>
+hipError_t launch_wide(const float *scores, int nq, int A, int k, int *ids, hipStream_t stream) {
+  constexpr int GS = 64 * E;
+  const int ngroups = (A + GS - 1) / GS;
+  // Published words per group, a power of two: enough that the union holds
+  // about 4k elements, at least 8 (a group then rarely holds more candidates
+  // than it publishes), at most 64 and WIDE_UCAP in all.  The caller keeps
+  // ngroups <= WIDE_UCAP / 4.
+  int M = 8;
+  while (M < 64 && M * ngroups < 4 * k) M *= 2;
+  while (M * ngroups > WIDE_UCAP) M /= 2;
+  void *ws = nullptr;
+  hipError_t e = workspace(stream, size_t(nq) * ngroups * M * sizeof(uint64_t), &ws);
+  if (e != hipSuccess) return e;
+  uint64_t *tops = static_cast<uint64_t *>(ws);
+  group_tops_kernel<E><<<dim3((ngroups + 3) / 4, nq), 256, 0, stream>>>(scores, A, ngroups, M, tops);
+  wide_rank_kernel<E><<<dim3(WIDE_NB, nq), NT, 0, stream>>>(scores, A, k, ids, tops, ngroups, M);
+  return hipGetLastError();
+}
+
+template <int PER>
 hipError_t launch_topk(const float *scores, int nq, int A, int k, int *ids, hipStream_t stream) {
   topk_kernel<PER><<<nq, NT, 0, stream>>>(scores, A, k, ids);
   return hipGetLastError();
@@ -493,6 +858,14 @@ hipError_t launch_topk(const float *scores, int nq, int A, int k, int *ids, hipS
 
 hipError_t launch_block_topk(const float *scores, int nq, int A, int k, int *ids,
                              hipStream_t stream) {
+  // Few rows: spread each row over the GPU (group size grows with the row so
+  // that the published words stay within WIDE_UCAP).
+  // (ngroups <= WIDE_UCAP / 4: every group publishes at least 4 words.)
+  if (nq <= kWideMaxRows && A > 0 && A <= 2048 * 1024) {
+    if (A <= 2048 * 64) return launch_wide<1>(scores, nq, A, k, ids, stream);
+    if (A <= 2048 * 256) return launch_wide<4>(scores, nq, A, k, ids, stream);
+    return launch_wide<16>(scores, nq, A, k, ids, stream);
+  }
   // Register width from the active block count only: the smallest PER with
   // (PER + 1) * NT >= A; longer rows stream from memory on every pass.
   const int slots = (A + NT - 1) / NT;  // PER + 1 needed

@@ -45,7 +45,9 @@ def test_binding_covers_the_header():
         binding.QSA_OK, binding.QSA_ERR_NULL, binding.QSA_ERR_SHAPE, binding.QSA_ERR_K,
         binding.QSA_ERR_ALIGN, binding.QSA_ERR_LAUNCH)
     assert mac["QSA_TOPK_MAX_K"] == binding.TOPK_MAX_K
+    assert mac["QSA_TOPK_FEW_ROWS"] == binding.TOPK_FEW_ROWS
     assert mac["QSA_ERR_MODE"] == binding.QSA_ERR_MODE
+    assert mac["QSA_ERR_NOMEM"] == binding.QSA_ERR_NOMEM
     assert (mac["QSA_SCORES_AUTO"], mac["QSA_SCORES_FP32"], mac["QSA_SCORES_BF16X3"]) == (
         binding.QSA_SCORES_AUTO, binding.QSA_SCORES_FP32, binding.QSA_SCORES_BF16X3)
     assert mac["QSA_MAX_HEAD_DIM"] == binding.QSA_MAX_HEAD_DIM
@@ -68,7 +70,7 @@ def test_library_is_built_for_gfx950_only():
 
 
 def test_strerror(lib):
-    for code in range(7):
+    for code in range(8):
         assert binding.qsa_strerror(code)
     assert binding.qsa_strerror(0) == "success"
     assert binding.qsa_strerror(99) == "unknown status"

@@ -62,7 +62,23 @@ def check_scores(s, s64):
     return ratio
 
 
-def check_topk(scores, k):
+FEW_ROWS = 16  # QSA_TOPK_FEW_ROWS: batches up to this many rows take the whole-GPU path
+PATHS = ["few-rows", "per-row"]
+
+
+def rows_for_path(scores: np.ndarray, path: str) -> np.ndarray:
+    """The same rows as a batch that takes the given top-k path: at most
+    FEW_ROWS rows for the whole-GPU path, more than that (the rows repeated)
+    for the one-workgroup-per-row path."""
+    if path == "few-rows":
+        assert scores.shape[0] <= FEW_ROWS
+        return scores
+    reps = FEW_ROWS // scores.shape[0] + 1
+    return np.ascontiguousarray(np.tile(scores, (reps, 1)))
+
+
+def check_topk(scores, k, path="few-rows"):
+    scores = rows_for_path(np.ascontiguousarray(scores, np.float32), path)
     ids = gpu_topk(scores, k)
     want = ORC.topk(scores, k)
     if not np.array_equal(ids, want):
@@ -169,24 +185,65 @@ WIDTH_CASES = [
 ]
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("a,k", WIDTH_CASES)
-def test_topk_widths_random(a, k):
+def test_topk_widths_random(a, k, path):
     rng = np.random.default_rng(a + k)
     s = (rng.standard_normal((3, a)) * 20).astype(np.float32)
-    check_topk(s, k)
+    check_topk(s, k, path)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("a,k", WIDTH_CASES)
-def test_topk_widths_heavy_ties(a, k):
+def test_topk_widths_heavy_ties(a, k, path):
     rng = np.random.default_rng(a * 3 + k)
-    check_topk(tie_rows(rng, 2, a, 7), k)
+    check_topk(tie_rows(rng, 2, a, 7), k, path)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("a,k", [(10, 20), (1, 4096), (513, 600), (4000, 4096), (3, 4)])
-def test_topk_k_larger_than_row(a, k):
+def test_topk_k_larger_than_row(a, k, path):
     rng = np.random.default_rng(a)
-    ids = check_topk(tie_rows(rng, 2, a, 5), k)
+    ids = check_topk(tie_rows(rng, 2, a, 5), k, path)
     assert np.all(ids[:, a:] == -1)
+
+
+def clustered_rows(rng, a):
+    """Rows whose best scores crowd into a few places: the whole-GPU path's
+    groups holding more winners than they publish (re-read from the scores),
+    groups with nothing to offer, and ties at its bound."""
+    base = (rng.standard_normal(a) * 5).astype(np.float32)
+    rows = []
+    r = base.copy(); r[300:1100] += 100                       # one region holds every winner
+    rows.append(r)
+    r = base.copy(); r[::97] += 60; r[a // 2: a // 2 + 700] += 80   # sparse spikes + a block
+    rows.append(r)
+    rows.append(np.sort(base))                                # increasing: the tail wins
+    rows.append(np.sort(base)[::-1].copy())                   # decreasing: the head wins
+    r = np.round(base).astype(np.float32)                     # integers: thousands of ties
+    rows.append(r)
+    r = base.copy(); r[-3:] = 1e30                            # winners in the ragged last group
+    rows.append(r)
+    return np.ascontiguousarray(np.stack(rows).astype(np.float32))
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("a,k", [(1200, 64), (8193, 256), (32770, 512), (65538, 1024),
+                                  (100003, 2048), (5000, 4096)])
+def test_topk_clustered(a, k, path):
+    rng = np.random.default_rng(a)
+    ids = check_topk(clustered_rows(rng, a), k, path)
+    assert ids.shape[1] == k
+
+
+@pytest.mark.parametrize("nq", [1, 2, 5, 16, 17, 40])
+def test_topk_batch_sizes(nq):
+    # around the switch between the two paths
+    rng = np.random.default_rng(nq)
+    s = (rng.standard_normal((nq, 32770)) * 20).astype(np.float32)
+    s[:, 5] = 1e9  # a row-wide needle
+    ids = check_topk(s, 512, "few-rows" if nq <= FEW_ROWS else "per-row")
+    assert np.all(ids[:, 0] == 5)
 
 
 def test_topk_no_active_blocks(gpu):
@@ -197,7 +254,8 @@ def test_topk_no_active_blocks(gpu):
     assert np.all(ids.cpu().numpy() == -1)
 
 
-def test_topk_special_rows():
+@pytest.mark.parametrize("path", PATHS)
+def test_topk_special_rows(path):
     a = 5000
     rows = [
         np.full(a, 1.5, np.float32),                         # all equal
@@ -212,7 +270,7 @@ def test_topk_special_rows():
     ]
     s = np.ascontiguousarray(np.stack(rows).astype(np.float32))
     for k in (1, 7, 1000, 4096):
-        ids = check_topk(s, k)
+        ids = check_topk(s, k, path)[: s.shape[0]]
         assert topk_invariants(s, ids, k) == []
     ids = gpu_topk(s[3:4], 10)[0]
     assert ids.tolist() == list(range(10)), "-0.0 and +0.0 must tie (lower id first)"
