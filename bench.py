@@ -3,23 +3,30 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one full selection pass over one batch of synthetic input:
-qsa_block_scores then qsa_block_topk, through the C ABI, on the current torch
-stream.  Default workload: 256 prompt queries x 32,770 active blocks (a 131K
-context) in a 65,538-block (262,144-cell) capacity, 4 heads x 128, k = 512.
+A step is one full selection pass over one batch of synthetic input: one
+qsa_block_select call (scores, then the top-k of those scores) through the C
+ABI, on the current torch stream.  Default workload: 256 prompt queries x
+32,770 active blocks (a 131K context) in a 65,538-block (262,144-cell)
+capacity, 4 heads x 128, k = 512.
 
 Steps rotate over several input copies (different HBM buffers, same values) so
 that the block summaries read by each step are not still sitting in the 256 MB
 last-level cache from the previous one.  Inputs are resident in HBM before the
 timed region starts.  Prints ONE JSON line.
 
-Per-kernel durations come from HIP events recorded on the stream the kernels
-run on, around each launch inside the timed region; `roofline` reports the
-scorer (the dominant kernel) against the peak of the matrix-core type it
-runs on: fp32 MFMA with 2 * nq * A * heads * dim FLOP, or -- the default for
-prompts -- bf16 MFMA on the exact three-way split, whose method forms six bf16
-slice products per fp32 product (6 * 2 * nq * A * heads * dim FLOP); the
-fp32-equivalent rate is reported beside it.
+Two timed passes over the same K steps:
+  1. throughput: the K steps bracketed by a device synchronisation (and a HIP
+     event pair) on both sides, nothing else inside -- `ms_per_step`, `value`;
+  2. kernel durations: the same steps as the two separate calls
+     (qsa_block_scores, qsa_block_topk) with HIP events recorded on their
+     stream around each -- per-stage times and `roofline`.  (An event costs
+     a few microseconds of GPU time, so pass 1 carries none.)
+`roofline` reports the scorer (the dominant kernel) against the peak of the
+unit it runs on: fp32 MFMA with 2 * nq * A * heads * dim FLOP; bf16 MFMA on the
+exact three-way split (the prompt default), whose method forms six bf16 slice
+products per fp32 product (6 * 2 * nq * A * heads * dim FLOP), with the
+fp32-equivalent rate beside it; or HBM for the few-query dot-product kernel
+(bytes of the active summaries, the queries and the scores).
 
 The CPU baseline is the CPU oracle (FP64 scores, then a sort-based top-k of its
 fp32-rounded scores) timed on this host's cores over the same workload.
@@ -75,12 +82,10 @@ def parse_args():
 
 
 def source_digest(path: str) -> str:
+    """Hash of a kernel's source file (the counters are void once it changes)."""
     import hashlib
-    h = hashlib.sha256()
-    for name in (path, "qsa_internal.h"):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    with open(os.path.join(CSRC, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def read_traffic(path: str, workload: str):
@@ -140,14 +145,15 @@ def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; the selection path "
-                          "is not sharded across GPUs here (see the design notes)",
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the selection path "
+                          "is not sharded across GPUs",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch
 
-    from sparse_attention_kv_qsa_amd import binding, qsa_block_scores_ex, qsa_block_topk
+    from sparse_attention_kv_qsa_amd import (binding, qsa_block_scores_ex, qsa_block_select,
+                                             qsa_block_topk)
 
     binding.load_library()
     dev = torch.device("cuda:0")
@@ -175,17 +181,34 @@ def main():
     mode = args.scores_mode
 
     def step(c):
-        qsa_block_scores_ex(q_d[c], k_d[c], w.active, scores=s_d[c], mode=mode)
-        qsa_block_topk(s_d[c], w.k, ids=i_d[c])
+        if mode == "auto":
+            qsa_block_select(q_d[c], k_d[c], w.k, w.active, scores=s_d[c], ids=i_d[c])
+        else:
+            qsa_block_scores_ex(q_d[c], k_d[c], w.active, scores=s_d[c], mode=mode)
+            qsa_block_topk(s_d[c], w.k, ids=i_d[c])
 
     for it in range(args.warmup):
         step(it % ncopy)
     torch.cuda.synchronize()
 
+    # Pass 1: throughput of the hot path.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    p0.record()
+    for it in range(K):
+        step(it % ncopy)
+    p1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / K
+    value = w.nq * w.active / (wall / K)
+    gpu_ms_step = p0.elapsed_time(p1) / K
+
+    # Pass 2: per-kernel durations, events around the two separate calls.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
     for it in range(K):
         c = it % ncopy
         e0, e1, e2 = ev[it]
@@ -195,38 +218,37 @@ def main():
         qsa_block_topk(s_d[c], w.k, ids=i_d[c])
         e2.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
     score_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
     topk_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
-    ms_step = wall * 1e3 / K
-    value = w.nq * w.active / (wall / K)
 
     flop = 2.0 * w.nq * w.active * w.K  # fp32-equivalent FLOP of the scores
     score_avg_s = float(np.mean(score_ms)) * 1e-3
     # The kernel the library runs for this shape and mode (mirrors its dispatch).
-    if w.nq <= 8 and mode != "bf16x3":
+    gemv_ok = w.nq <= 8 and w.nq * -(-w.K // 256) <= 16
+    if gemv_ok and mode != "bf16x3":
         path = "gemv"
     else:
         path = "bf16x3" if mode in ("auto", "bf16x3") else "fp32"
     extra = {}
+    select_bytes = 4.0 * (w.active * w.K + w.nq * w.K + 2 * w.nq * w.active + w.nq * w.k)
     if path == "gemv":
         nbytes = 4.0 * (w.active * w.K + w.nq * w.K + w.nq * w.active)
         gbs = nbytes / score_avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "scores_gemv_kernel"}
     elif path == "fp32":
         tf = flop / score_avg_s / 1e12
         roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_MFMA_TFLOPS, 4),
-                "traffic": read_traffic("fp32", w.name)}
+                "traffic": read_traffic("fp32", w.name), "kernel": "scores_mfma_kernel"}
     else:
         # The split method forms six bf16 slice products per fp32 product: its
         # algorithmic work on the bf16 matrix cores is 6 * 2 * nq * A * K.
         tf = 6.0 * flop / score_avg_s / 1e12
         roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_MFMA_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_MFMA_TFLOPS, 4),
-                "traffic": read_traffic("bf16x3", w.name)}
+                "traffic": read_traffic("bf16x3", w.name), "kernel": "scores_bf16x3_kernel"}
         extra = {"scores_fp32_equiv_tflops": round(flop / score_avg_s / 1e12, 2),
                  "scores_frac_of_fp32_mfma_peak": round(flop / score_avg_s / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)}
     topk_bytes = 4.0 * (w.nq * w.active + w.nq * w.k)
@@ -251,9 +273,13 @@ def main():
                          f"({w.capacity}-block capacity), {w.heads} heads x {w.dim}, k={w.k}"),
             "nq": w.nq, "active_blocks": w.active, "capacity_blocks": w.capacity,
             "heads": w.heads, "dim": w.dim, "k": w.k, "input_copies": ncopy,
-            "scores_mode": mode,
+            "scores_mode": mode, "step": "qsa_block_select" if mode == "auto" else
+            "qsa_block_scores_ex + qsa_block_topk",
         },
         "stages": {
+            "gpu_ms_per_step": round(gpu_ms_step, 5),
+            "step_hbm_gbs": round(select_bytes / (ms_step * 1e-3) / 1e9, 1),
+            "step_hbm_frac": round(select_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "scores_ms": round(float(np.mean(score_ms)), 5),
             "scores_ms_median": round(float(np.median(score_ms)), 5),
             "topk_ms": round(float(np.mean(topk_ms)), 5),

@@ -136,6 +136,26 @@ int qsa_block_topk(const float *scores, int nq, int active_blocks, int k, int *i
 int qsa_block_scores_ex(const float *q, const float *kblk, int nq, int heads, int dim,
                         int active_blocks, float *scores, int mode, void *stream);
 
+/*
+ * qsa_block_select -- both steps in one call: the scores of
+ * qsa_block_scores (precision mode QSA_SCORES_AUTO) into `scores`, and the
+ * top-k ids of qsa_block_topk on exactly those scores into `ids`.
+ *
+ * Results are identical to the two separate calls.  For few queries (nq <=
+ * 8, the decode regime, with active_blocks <= 131072) the scoring kernel
+ * also publishes, for every group of 64 consecutive blocks, the group's best
+ * (score, id) pairs, which the top-k would otherwise read back in a launch
+ * of its own -- one launch fewer on the latency-bound decode path (page
+ * "#3108 perf(hip): optimize exact QSA block scoring and top-k selection on
+ * gfx12", decode table: the selection, not the scoring, dominated decode).
+ *
+ * Arguments, layouts, alignment and errors as for the two calls.  k == 0
+ * computes the scores only; active_blocks == 0 writes ids of -1 only;
+ * nq == 0 is a successful no-op.
+ */
+int qsa_block_select(const float *q, const float *kblk, int nq, int heads, int dim,
+                     int active_blocks, int k, float *scores, int *ids, void *stream);
+
 /* Human-readable text of a status code (a static string; never NULL). */
 const char *qsa_strerror(int status);
 

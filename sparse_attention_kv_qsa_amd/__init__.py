@@ -13,7 +13,8 @@ from .synth import WORKLOADS, HEADLINE, Workload, make_batch, make_random, finge
 def __getattr__(name):
     # The binding loads libqsa.so (and torch) on first use only, so the
     # generator can be imported on hosts without the library.
-    if name in ("qsa_block_scores", "qsa_block_scores_ex", "qsa_block_topk", "qsa_strerror",
+    if name in ("qsa_block_scores", "qsa_block_scores_ex", "qsa_block_topk", "qsa_block_select",
+                "qsa_strerror", "TOPK_FEW_ROWS",
                 "QSAError", "SCORE_MODES",
                 "load_library", "library_path", "TOPK_MAX_K", "block_scores", "block_topk"):
         from . import binding

@@ -32,6 +32,7 @@ SIGNATURES = {
     "qsa_block_scores": (_I, [_VP, _VP, _I, _I, _I, _I, _VP, _VP]),
     "qsa_block_scores_ex": (_I, [_VP, _VP, _I, _I, _I, _I, _VP, _I, _VP]),
     "qsa_block_topk": (_I, [_VP, _I, _I, _I, _VP, _VP]),
+    "qsa_block_select": (_I, [_VP, _VP, _I, _I, _I, _I, _I, _VP, _VP, _VP]),
     "qsa_strerror": (ctypes.c_char_p, [_I]),
 }
 
@@ -116,6 +117,38 @@ def qsa_block_scores(q: torch.Tensor, kblk: torch.Tensor, active_blocks: int | N
                      scores: torch.Tensor | None = None) -> torch.Tensor:
     """Scores [nq, active_blocks] with the library's default precision mode."""
     return qsa_block_scores_ex(q, kblk, active_blocks, scores, QSA_SCORES_AUTO)
+
+
+def qsa_block_select(q: torch.Tensor, kblk: torch.Tensor, k: int, active_blocks: int | None = None,
+                     scores: torch.Tensor | None = None, ids: torch.Tensor | None = None):
+    """(scores [nq, active_blocks], ids [nq, k]) in one call: the scores of
+    qsa_block_scores and the top-k of qsa_block_topk on them."""
+    _require_gpu_f32("q", q, 3)
+    _require_gpu_f32("kblk", kblk, 3)
+    nq, heads, dim = q.shape
+    if kblk.shape[1:] != (heads, dim) or kblk.device != q.device:
+        raise ValueError("kblk must be [C, heads, dim] on q's device")
+    a = kblk.shape[0] if active_blocks is None else int(active_blocks)
+    if not 0 <= a <= kblk.shape[0]:
+        raise ValueError(f"active_blocks={a} outside [0, {kblk.shape[0]}]")
+    k = int(k)
+    if scores is None:
+        scores = torch.empty((nq, a), dtype=torch.float32, device=q.device)
+    elif tuple(scores.shape) != (nq, a) or scores.device != q.device or \
+            scores.dtype != torch.float32 or not scores.is_contiguous():
+        raise ValueError(f"scores must be a contiguous float32 [{nq}, {a}] tensor on q's device")
+    if ids is None:
+        ids = torch.empty((nq, max(k, 0)), dtype=torch.int32, device=q.device)
+    elif tuple(ids.shape) != (nq, k) or ids.device != q.device or ids.dtype != torch.int32 or \
+            not ids.is_contiguous():
+        raise ValueError(f"ids must be a contiguous int32 [{nq}, {k}] tensor on q's device")
+    with torch.cuda.device(q.device):
+        st = load_library().qsa_block_select(q.data_ptr(), kblk.data_ptr(), nq, heads, dim, a, k,
+                                             scores.data_ptr(), ids.data_ptr(),
+                                             _stream_handle(q.device))
+    if st != QSA_OK:
+        raise QSAError(st, "qsa_block_select")
+    return scores, ids
 
 
 def qsa_block_topk(scores: torch.Tensor, k: int, ids: torch.Tensor | None = None) -> torch.Tensor:

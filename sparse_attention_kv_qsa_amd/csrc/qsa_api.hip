@@ -58,6 +58,28 @@ extern "C" int qsa_block_topk(const float *scores, int nq, int active_blocks, in
                                               static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int qsa_block_select(const float *q, const float *kblk, int nq, int heads, int dim,
+                                int active_blocks, int k, float *scores, int *ids, void *stream) {
+  if (nq < 0 || heads < 0 || dim < 0 || active_blocks < 0) return QSA_ERR_SHAPE;
+  const int64_t K = int64_t(heads) * dim;
+  if (K < 4 || K % 4 != 0 || K > QSA_MAX_HEAD_DIM) return QSA_ERR_SHAPE;
+  if (k < 0 || k > QSA_TOPK_MAX_K) return QSA_ERR_K;
+  if (nq == 0 || (k == 0 && active_blocks == 0)) return QSA_OK;
+  if (active_blocks > 0 && (!q || !kblk || !scores)) return QSA_ERR_NULL;
+  if (k > 0 && !ids) return QSA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(kblk, 16) || !aligned(scores, 4) || !aligned(ids, 4))
+    return QSA_ERR_ALIGN;
+  (void)hipGetLastError();  // start from a clean launch status
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (k == 0)
+    return launch_status(
+        qsa::launch_block_scores(q, kblk, nq, int(K), active_blocks, scores, qsa::kScoresAuto, s));
+  if (active_blocks == 0)
+    return launch_status(qsa::launch_block_topk(scores, nq, 0, k, ids, s));
+  return launch_status(
+      qsa::launch_block_select(q, kblk, nq, int(K), active_blocks, k, scores, ids, s));
+}
+
 extern "C" const char *qsa_strerror(int status) {
   switch (status) {
     case QSA_OK:

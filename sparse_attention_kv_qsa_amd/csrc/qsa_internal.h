@@ -45,4 +45,22 @@ hipError_t workspace(hipStream_t stream, size_t bytes, void **ptr);
 hipError_t launch_block_topk(const float *scores, int nq, int active_blocks, int k,
                              int *ids, hipStream_t stream);
 
+// Scores and top-k ids in one call (k >= 1).  For few queries whose scores
+// take the dot-product kernel, the scorer also publishes each 64-block
+// group's best rank words, so the selection needs one more launch instead
+// of two; otherwise the two steps run as in separate calls.
+hipError_t launch_block_select(const float *q, const float *kblk, int nq, int K,
+                               int active_blocks, int k, float *scores, int *ids,
+                               hipStream_t stream);
+
+// Pieces of the fused path.  The whole-GPU top-k groups rows into 64-element
+// groups that publish M rank words each (tops[nq][ngroups][M]).
+constexpr int kWideMaxBlocksFused = 2048 * 64;  // groups of 64: ngroups <= 2048
+bool gemv_fits(int nq, int K);
+int wide_words_per_group(int ngroups, int k);
+hipError_t launch_gemv_tops(const float *q, const float *kblk, int nq, int K, int A,
+                            float *scores, uint64_t *tops, int M, hipStream_t stream);
+hipError_t launch_wide_rank(const float *scores, int nq, int A, int k, int *ids,
+                            const uint64_t *tops, int M, hipStream_t stream);
+
 }  // namespace qsa

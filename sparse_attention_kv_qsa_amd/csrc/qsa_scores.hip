@@ -19,6 +19,7 @@
 
 #include <algorithm>
 
+#include "qsa_device.h"
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -89,6 +90,102 @@ __global__ __launch_bounds__(256) void scores_gemv_kernel(const float *__restric
       const int64_t r = row0 + u;
       if (lane == u * NQ + n && r < A && n < nq) scores[int64_t(n) * A + r] = p[u][n];
     }
+}
+
+// ---------------------------------------------------------------------------
+// Decode scorer with the first step of the whole-GPU top-k fused in.  A
+// workgroup of 16 waves scores one group of 64 consecutive blocks (wave w:
+// blocks 4w .. 4w+3, U at a time, with exactly the arithmetic of
+// scores_gemv_kernel), stores the scores, and then wave n publishes query
+// n's M best rank words of the group -- what the top-k's first kernel would
+// compute from the stored scores, without reading them back.
+// ---------------------------------------------------------------------------
+template <int NQ, int NC, int U>
+__global__ __launch_bounds__(1024) void scores_gemv_tops_kernel(const float *__restrict__ q,
+                                                                const float *__restrict__ kblk,
+                                                                int nq, int K, int A,
+                                                                float *__restrict__ scores,
+                                                                uint64_t *__restrict__ tops,
+                                                                int ngroups, int M) {
+  __shared__ float sc[NQ][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t g = blockIdx.x;
+
+  f4 qf[NQ][NC];
+#pragma unroll
+  for (int n = 0; n < NQ; ++n)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int e = 4 * (c * 64 + lane);
+      qf[n][c] = (n < nq && e < K) ? load_f4(q + int64_t(n) * K + e) : f4{0.f, 0.f, 0.f, 0.f};
+    }
+
+#pragma unroll
+  for (int it = 0; it < 4 / U; ++it) {
+    const int64_t row0 = g * 64 + wave * 4 + it * U;
+    f4 kf[U][NC];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int e = 4 * (c * 64 + lane);
+        const int64_t r = row0 + u;
+        kf[u][c] = (r < A && e < K) ? load_f4(kblk + r * K + e) : f4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) {
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          acc = __builtin_fmaf(qf[n][c].x, kf[u][c].x, acc);
+          acc = __builtin_fmaf(qf[n][c].y, kf[u][c].y, acc);
+          acc = __builtin_fmaf(qf[n][c].z, kf[u][c].z, acc);
+          acc = __builtin_fmaf(qf[n][c].w, kf[u][c].w, acc);
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+        const int64_t r = row0 + u;
+        if (lane == u * NQ + n && r < A && n < nq) scores[int64_t(n) * A + r] = acc;
+        if (lane == 0) sc[n][wave * 4 + it * U + u] = acc;
+      }
+  }
+  __syncthreads();
+  if (wave < nq) {
+    const uint32_t id = uint32_t(g * 64 + lane);
+    const uint32_t key = id < uint32_t(A) ? score_key(__float_as_uint(sc[wave][lane])) : 0u;
+    publish_group_tops(key, id, M, tops + (int64_t(wave) * ngroups + g) * M);
+  }
+}
+
+template <int NQ, int NC>
+hipError_t launch_gemv_tops_nc(const float *q, const float *kblk, int nq, int K, int A,
+                               float *scores, uint64_t *tops, int M, hipStream_t stream) {
+  constexpr int U = NC >= 8 ? 1 : NC >= 4 ? 2 : 4;
+  const int ngroups = (A + 63) / 64;
+  scores_gemv_tops_kernel<NQ, NC, U><<<ngroups, 1024, 0, stream>>>(q, kblk, nq, K, A, scores, tops,
+                                                                 ngroups, M);
+  return hipGetLastError();
+}
+
+template <int NQ>
+hipError_t launch_gemv_tops_q(const float *q, const float *kblk, int nq, int K, int A,
+                              float *scores, uint64_t *tops, int M, hipStream_t stream) {
+  const int nc = (K + 255) / 256;
+  if (nc <= 1) return launch_gemv_tops_nc<NQ, 1>(q, kblk, nq, K, A, scores, tops, M, stream);
+  if (nc <= 2) return launch_gemv_tops_nc<NQ, 2>(q, kblk, nq, K, A, scores, tops, M, stream);
+  if constexpr (NQ <= 4) {
+    if (nc <= 4) return launch_gemv_tops_nc<NQ, 4>(q, kblk, nq, K, A, scores, tops, M, stream);
+  }
+  if constexpr (NQ <= 2) {
+    if (nc <= 8) return launch_gemv_tops_nc<NQ, 8>(q, kblk, nq, K, A, scores, tops, M, stream);
+  }
+  if constexpr (NQ <= 1) {
+    if (nc <= 16) return launch_gemv_tops_nc<NQ, 16>(q, kblk, nq, K, A, scores, tops, M, stream);
+  }
+  return hipErrorInvalidValue;  // the caller checks gemv_fits first
 }
 
 // ---------------------------------------------------------------------------
@@ -310,6 +407,8 @@ hipError_t launch_gemv_nc(const float *q, const float *kblk, int nq, int K, int 
   return hipErrorInvalidValue;  // caller routes these shapes to the MFMA kernel
 }
 
+}  // namespace
+
 // Whether the GEMV kernel keeps this (nq, K) in registers (NQ * NC <= 16).
 bool gemv_fits(int nq, int K) {
   if (nq > kGemvMaxQueries) return false;
@@ -319,7 +418,15 @@ bool gemv_fits(int nq, int K) {
   return nqp * ncp <= 16;
 }
 
-}  // namespace
+
+hipError_t launch_gemv_tops(const float *q, const float *kblk, int nq, int K, int A,
+                            float *scores, uint64_t *tops, int M, hipStream_t stream) {
+  if (!gemv_fits(nq, K)) return hipErrorInvalidValue;
+  if (nq <= 1) return launch_gemv_tops_q<1>(q, kblk, nq, K, A, scores, tops, M, stream);
+  if (nq <= 2) return launch_gemv_tops_q<2>(q, kblk, nq, K, A, scores, tops, M, stream);
+  if (nq <= 4) return launch_gemv_tops_q<4>(q, kblk, nq, K, A, scores, tops, M, stream);
+  return launch_gemv_tops_q<8>(q, kblk, nq, K, A, scores, tops, M, stream);
+}
 
 hipError_t launch_block_scores_fp32(const float *q, const float *kblk, int nq, int K, int A,
                                     float *scores, hipStream_t stream) {

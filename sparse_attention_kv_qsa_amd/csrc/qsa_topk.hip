@@ -29,6 +29,7 @@
 //      through LDS above that.
 #include <hip/hip_runtime.h>
 
+#include "qsa_device.h"
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -52,89 +53,6 @@ struct TopkShared {
   uint32_t bid[MAXK];          // ... and ids, sorted into rank order
   uint32_t extra[NT];          // each thread's last key slot (kept in LDS, not VGPRs)
 };
-
-// Order-preserving map of an fp32 score (given as its bits) to uint32: a
-// larger score gives a larger key.  -0.0 is folded onto +0.0.  Key 0 is kept
-// free as the "no block" sentinel; the one score that would map there is a
-// NaN (whose rank is unspecified), so it moves to 1.
-__device__ __forceinline__ uint32_t score_key(uint32_t u) {
-  if (u == 0x80000000u) u = 0u;
-  const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return key == 0u ? 1u : key;
-}
-
-// v of lane (lane ^ S) for a power of two S < 64.  Strides up to 8 stay on
-// the VALU (DPP quad permutes, row shifts under bank masks, a row rotate); 16
-// and 32 cross rows through the LDS crossbar.  S must be a compile-time
-// constant after unrolling: a runtime switch here costs a dozen scalar
-// branches per exchange.
-template <int S>
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
-  const int x = int(v);
-  if constexpr (S == 1) {
-    return uint32_t(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
-  } else if constexpr (S == 2) {
-    return uint32_t(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
-  } else if constexpr (S == 4) {
-    // banks 0 and 2 (lane bit 2 clear) read lane + 4, banks 1 and 3 read lane - 4
-    const int r = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0x5, false);  // row_shl:4
-    return uint32_t(__builtin_amdgcn_update_dpp(r, x, 0x114, 0xF, 0xA, false));  // row_shr:4
-  } else if constexpr (S == 8) {
-    return uint32_t(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));  // row_ror:8
-  } else {
-    return uint32_t(__shfl_xor(x, S, 64));
-  }
-}
-
-// One compare-exchange step of a bitonic network held one element per lane,
-// for a partner in the same wave (STRIDE < 64).  `pos` is the element's
-// position; blocks whose position has the SIZE bit clear run in rank order.
-// Ties (identical pairs) never swap.
-template <int SIZE, int STRIDE, class Before>
-__device__ __forceinline__ void bitonic_lane_step(uint32_t &key, uint32_t &id, int pos,
-                                                  Before &&before) {
-  const uint32_t pk = lane_xor<STRIDE>(key);
-  const uint32_t pi = lane_xor<STRIDE>(id);
-  // Branch-free: both orders are evaluated and selected with bit operations
-  // (a conditional here compiles to divergent branches on every step).
-  const bool take_first = ((pos & STRIDE) == 0) == ((pos & SIZE) == 0);
-  const bool take = (take_first & before(pk, pi, key, id)) | (!take_first & before(key, id, pk, pi));
-  key = take ? pk : key;
-  id = take ? pi : id;
-}
-
-// All steps of stage SIZE with strides below 64 (STRIDE = min(SIZE, 64) / 2 down to 1).
-template <int SIZE, int STRIDE, class Before>
-__device__ __forceinline__ void bitonic_lane_stage(uint32_t &key, uint32_t &id, int pos,
-                                                   Before &&before) {
-  if constexpr (STRIDE >= 1) {
-    bitonic_lane_step<SIZE, STRIDE>(key, id, pos, before);
-    bitonic_lane_stage<SIZE, STRIDE / 2>(key, id, pos, before);
-  }
-}
-
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave, on DPP lane shifts:
-// four shifts within each row of 16 lanes, then the row totals carried
-// forward with row broadcasts (lane 15 -> row 1 and 3, lane 31 -> rows 2, 3).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  int x = int(v);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
-  return uint32_t(x);
-}
-
-// Sum over the wave, the same in every lane.
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-  return __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
-}
 
 // Given the histogram of the current digit in sh.hsub (complete: the caller
 // has passed a barrier), find the digit d* holding the kr-th largest
@@ -538,9 +456,6 @@ constexpr int WIDE_CCAP = 4096;  // LDS candidate capacity
 constexpr int WIDE_UCAP = 8192;  // published words per row, at most
 constexpr int WIDE_RCAP = 1024;  // rich groups listed (more: the one-workgroup fallback)
 
-__device__ __forceinline__ uint64_t rank_word(uint32_t key, uint32_t id) {
-  return (uint64_t(key) << 32) | uint64_t(~id);
-}
 
 // Wave maximum of a rank word held as (key, ~id) halves, using lane_xor
 // (DPP within rows of 16 lanes).
@@ -585,18 +500,7 @@ __global__ __launch_bounds__(256) void group_tops_kernel(const float *__restrict
   uint64_t *dst = tops + (int64_t(row) * ngroups + g) * M;
   if constexpr (E == 1) {
     const uint32_t id = uint32_t(g * GS + lane);
-    uint32_t key = id < uint32_t(A) ? score_key(raw[0]) : 0u;
-    uint32_t nid = ~id;  // larger ~id = lower id = earlier in rank order
-    auto first = [](uint32_t ka, uint32_t ia, uint32_t kb, uint32_t ib) {
-      return (ka > kb) | ((ka == kb) & (ia > ib));
-    };
-    bitonic_lane_stage<2, 1>(key, nid, lane, first);
-    bitonic_lane_stage<4, 2>(key, nid, lane, first);
-    bitonic_lane_stage<8, 4>(key, nid, lane, first);
-    bitonic_lane_stage<16, 8>(key, nid, lane, first);
-    bitonic_lane_stage<32, 16>(key, nid, lane, first);
-    bitonic_lane_stage<64, 32>(key, nid, lane, first);
-    if (lane < M) dst[lane] = key ? (uint64_t(key) << 32) | nid : 0ull;
+    publish_group_tops(id < uint32_t(A) ? score_key(raw[0]) : 0u, id, M, dst);
   } else {
     uint64_t v[E];
 #pragma unroll
@@ -832,13 +736,7 @@ template <int E>
 hipError_t launch_wide(const float *scores, int nq, int A, int k, int *ids, hipStream_t stream) {
   constexpr int GS = 64 * E;
   const int ngroups = (A + GS - 1) / GS;
-  // Published words per group, a power of two: enough that the union holds
-  // about 4k elements, at least 8 (a group then rarely holds more candidates
-  // than it publishes), at most 64 and WIDE_UCAP in all.  The caller keeps
-  // ngroups <= WIDE_UCAP / 4.
-  int M = 8;
-  while (M < 64 && M * ngroups < 4 * k) M *= 2;
-  while (M * ngroups > WIDE_UCAP) M /= 2;
+  const int M = wide_words_per_group(ngroups, k);
   void *ws = nullptr;
   hipError_t e = workspace(stream, size_t(nq) * ngroups * M * sizeof(uint64_t), &ws);
   if (e != hipSuccess) return e;
@@ -855,6 +753,23 @@ hipError_t launch_topk(const float *scores, int nq, int A, int k, int *ids, hipS
 }
 
 }  // namespace
+
+int wide_words_per_group(int ngroups, int k) {
+  // A power of two: enough that the union holds about 4k elements, at least
+  // 8 (a group then rarely holds more candidates than it publishes), at
+  // most 64 and WIDE_UCAP in all.  Callers keep ngroups <= WIDE_UCAP / 4.
+  int M = 8;
+  while (M < 64 && M * ngroups < 4 * k) M *= 2;
+  while (M > 1 && M * ngroups > WIDE_UCAP) M /= 2;
+  return M;
+}
+
+hipError_t launch_wide_rank(const float *scores, int nq, int A, int k, int *ids,
+                            const uint64_t *tops, int M, hipStream_t stream) {
+  const int ngroups = (A + 63) / 64;
+  wide_rank_kernel<1><<<dim3(WIDE_NB, nq), NT, 0, stream>>>(scores, A, k, ids, tops, ngroups, M);
+  return hipGetLastError();
+}
 
 hipError_t launch_block_topk(const float *scores, int nq, int A, int k, int *ids,
                              hipStream_t stream) {

@@ -33,8 +33,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert header_entry_points() == ["qsa_block_scores", "qsa_block_scores_ex", "qsa_block_topk",
-                                     "qsa_strerror"]
+    assert header_entry_points() == ["qsa_block_scores", "qsa_block_scores_ex", "qsa_block_select",
+                                     "qsa_block_topk", "qsa_strerror"]
 
 
 def test_binding_covers_the_header():
@@ -122,6 +122,25 @@ def test_block_scores_ex_mode_check(lib, mode, status):
 ])
 def test_block_topk_argument_checks(lib, args, status):
     assert lib.qsa_block_topk(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    # q, kblk, nq, heads, dim, active, k, scores, ids
+    ((P16, P16, -1, 4, 128, 10, 4, P16, P16), binding.QSA_ERR_SHAPE),
+    ((P16, P16, 1, 3, 3, 10, 4, P16, P16), binding.QSA_ERR_SHAPE),
+    ((P16, P16, 1, 4, 128, -1, 4, P16, P16), binding.QSA_ERR_SHAPE),
+    ((P16, P16, 1, 4, 128, 10, -1, P16, P16), binding.QSA_ERR_K),
+    ((P16, P16, 1, 4, 128, 10, 4097, P16, P16), binding.QSA_ERR_K),
+    ((None, P16, 1, 4, 128, 10, 4, P16, P16), binding.QSA_ERR_NULL),
+    ((P16, P16, 1, 4, 128, 10, 4, None, P16), binding.QSA_ERR_NULL),
+    ((P16, P16, 1, 4, 128, 10, 4, P16, None), binding.QSA_ERR_NULL),
+    ((P4, P16, 1, 4, 128, 10, 4, P16, P16), binding.QSA_ERR_ALIGN),
+    ((P16, P16, 1, 4, 128, 10, 4, P16, P16 + 2), binding.QSA_ERR_ALIGN),
+    ((None, None, 0, 4, 128, 10, 4, None, None), binding.QSA_OK),   # nq = 0: no-op
+    ((None, None, 2, 4, 128, 0, 0, None, None), binding.QSA_OK),    # nothing to do
+])
+def test_block_select_argument_checks(lib, args, status):
+    assert lib.qsa_block_select(*args, None) == status
 
 
 def test_binding_refuses_cpu_tensors():

@@ -282,25 +282,78 @@ def test_topk_deterministic():
     assert np.array_equal(gpu_topk(s, 800), gpu_topk(s, 800))
 
 
+# ------------------------------------------------------------ select ----
+
+SELECT_CASES = [  # nq, heads, dim, active, k  (nq <= 8 with K <= 4096/nq fuse; the rest do not)
+    (1, 4, 64, 512, 64), (1, 4, 128, 32770, 512), (1, 4, 128, 1000, 1000), (2, 4, 128, 5000, 100),
+    (3, 2, 128, 777, 50), (8, 4, 128, 8193, 256), (1, 8, 256, 3000, 128), (1, 16, 256, 640, 64),
+    (4, 4, 256, 2049, 300), (5, 2, 64, 65, 7), (1, 1, 4, 70, 5), (1, 4, 128, 63, 4096),
+    (9, 4, 128, 3000, 256), (1, 4, 128, 131073, 64), (40, 4, 128, 2000, 100), (8, 8, 128, 300, 30),
+]
+
+
+@pytest.mark.parametrize("nq,heads,dim,active,k", SELECT_CASES)
+def test_select_matches_separate_calls(nq, heads, dim, active, k):
+    from sparse_attention_kv_qsa_amd import qsa_block_scores, qsa_block_select, qsa_block_topk
+    q, kb = synth.make_random(nq, heads, dim, active, capacity=active + 3, seed=nq * 31 + active)
+    qt, kt = torch.from_numpy(q).cuda(), torch.from_numpy(kb).cuda()
+    s_sel, i_sel = qsa_block_select(qt, kt, k, active)
+    s_sep = qsa_block_scores(qt, kt, active)
+    i_sep = qsa_block_topk(s_sep, k)
+    torch.cuda.synchronize()
+    s_sel, i_sel, s_sep, i_sep = (x.cpu().numpy() for x in (s_sel, i_sel, s_sep, i_sep))
+    assert np.array_equal(s_sel, s_sep), "select's scores differ from qsa_block_scores"
+    assert np.array_equal(i_sel, i_sep), "select's ids differ from qsa_block_topk"
+    check_scores(s_sel, ORC.scores_f64(q, kb, active))
+    assert np.array_equal(i_sel, ORC.topk(s_sel, k))
+
+
+def test_select_edges(gpu):
+    from sparse_attention_kv_qsa_amd import qsa_block_select
+    q, kb = synth.make_random(2, 4, 128, 300, capacity=303, seed=9)
+    qt, kt = torch.from_numpy(q).cuda(), torch.from_numpy(kb).cuda()
+    # k = 0: scores only, ids untouched
+    ids = torch.full((2, 0), 7, dtype=torch.int32, device="cuda")
+    s, _ = qsa_block_select(qt, kt, 0, 300, ids=ids)
+    torch.cuda.synchronize()
+    check_scores(s.cpu().numpy(), ORC.scores_f64(q, kb, 300))
+    # no active blocks: all -1
+    ids = torch.full((2, 5), 7, dtype=torch.int32, device="cuda")
+    _, ids = qsa_block_select(qt, kt, 5, 0, ids=ids)
+    torch.cuda.synchronize()
+    assert np.all(ids.cpu().numpy() == -1)
+    # mass ties through the fused path: every summary identical
+    kb_same = np.ascontiguousarray(np.broadcast_to(kb[:1], (5000, 4, 128)))
+    s, ids = qsa_block_select(qt, torch.from_numpy(kb_same).cuda(), 100, 5000)
+    torch.cuda.synchronize()
+    s = s.cpu().numpy()
+    assert np.all(s == s[:, :1])
+    assert np.array_equal(ids.cpu().numpy(), np.tile(np.arange(100, dtype=np.int32), (2, 1)))
+
+
 # ------------------------------------------------- full workloads ----
 
 SAMPLE_ROWS = 6
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("mode", ["auto", "fp32"])
+@pytest.mark.parametrize("mode", ["auto", "fp32", "select"])
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_workload_parity(name, mode):
     w = synth.WORKLOADS[name]
     print(f"\n[workload {name} {mode}] nq={w.nq} A={w.active} C={w.capacity} K={w.K} k={w.k}",
           flush=True)
     bt = synth.make_batch(w)
-    from sparse_attention_kv_qsa_amd import qsa_block_scores_ex, qsa_block_topk
+    from sparse_attention_kv_qsa_amd import qsa_block_scores_ex, qsa_block_select, qsa_block_topk
     qt, kt = torch.from_numpy(bt.q).cuda(), torch.from_numpy(bt.kblk).cuda()
-    s_t = qsa_block_scores_ex(qt, kt, w.active, mode=mode)
-    ids_t = qsa_block_topk(s_t, w.k)
-    s_t2 = qsa_block_scores_ex(qt, kt, w.active, mode=mode)
-    ids_t2 = qsa_block_topk(s_t2, w.k)
+    if mode == "select":
+        s_t, ids_t = qsa_block_select(qt, kt, w.k, w.active)
+        s_t2, ids_t2 = qsa_block_select(qt, kt, w.k, w.active)
+    else:
+        s_t = qsa_block_scores_ex(qt, kt, w.active, mode=mode)
+        ids_t = qsa_block_topk(s_t, w.k)
+        s_t2 = qsa_block_scores_ex(qt, kt, w.active, mode=mode)
+        ids_t2 = qsa_block_topk(s_t2, w.k)
     torch.cuda.synchronize()
     s, ids = s_t.cpu().numpy(), ids_t.cpu().numpy()
     assert np.array_equal(s, s_t2.cpu().numpy()) and np.array_equal(ids, ids_t2.cpu().numpy())
