@@ -23,8 +23,10 @@ __device__ __forceinline__ uint64_t rank_word(uint32_t key, uint32_t id) {
 }
 
 // v of lane (lane ^ S) for a power of two S < 64.  Strides up to 8 stay on
-// the VALU (DPP quad permutes, row shifts under bank masks, a row rotate); 16
-// and 32 cross rows through the LDS crossbar.  S must be a compile-time
+// DPP (quad permutes, row shifts under bank masks, a row rotate); 16 and 32
+// use gfx950's lane-swap instructions (v_permlane16_swap / v_permlane32_swap:
+// with both operands x, lanes with the S bit set find the partner's value in
+// the first result and the others in the second).  S must be a compile-time
 // constant after unrolling: a runtime switch here costs a dozen scalar
 // branches per exchange.
 template <int S>
@@ -40,6 +42,10 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
     return uint32_t(__builtin_amdgcn_update_dpp(r, x, 0x114, 0xF, 0xA, false));  // row_shr:4
   } else if constexpr (S == 8) {
     return uint32_t(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));  // row_ror:8
+  } else if constexpr (S == 16 || S == 32) {
+    const auto r = S == 32 ? __builtin_amdgcn_permlane32_swap(v, v, false, false)
+                           : __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & S) ? r[0] : r[1];
   } else {
     return uint32_t(__shfl_xor(x, S, 64));
   }
@@ -69,6 +75,23 @@ __device__ __forceinline__ void bitonic_lane_stage(uint32_t &key, uint32_t &id, 
   if constexpr (STRIDE >= 1) {
     bitonic_lane_step<SIZE, STRIDE>(key, id, pos, before);
     bitonic_lane_stage<SIZE, STRIDE / 2>(key, id, pos, before);
+  }
+}
+
+// Bitonic network over 64-bit rank words (a larger word ranks first), one per
+// lane: stage SIZE's in-wave steps, strides min(SIZE, 64)/2 down to 1.  A
+// lane whose position has the SIZE bit clear keeps the larger word of each
+// pair when it is the pair's lower position, so those blocks end in
+// descending order.
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_word_stage(uint64_t &w, int pos) {
+  if constexpr (STRIDE >= 1) {
+    const uint32_t lo = lane_xor<STRIDE>(uint32_t(w));
+    const uint32_t hi = lane_xor<STRIDE>(uint32_t(w >> 32));
+    const uint64_t p = (uint64_t(hi) << 32) | lo;
+    const bool keep_larger = ((pos & STRIDE) == 0) == ((pos & SIZE) == 0);
+    w = ((p > w) == keep_larger) ? p : w;
+    bitonic_word_stage<SIZE, STRIDE / 2>(w, pos);
   }
 }
 

@@ -16,17 +16,18 @@
 //      ceil(k/16)-th; the smallest offer is <= the k-th largest key.  Only
 //      keys at or above the bound can win; they are compacted into LDS (a few
 //      percent of an N(0,1) row at k/A = 1/64).
-//   3. radix select on the candidates: up to four MSB-first passes over 8-bit
-//      digits, each a 256-bin LDS histogram (one sub-histogram per wave), a
-//      suffix scan to find the bin holding the k-th largest key, and the
-//      prefix grows by that digit; a pass whose bin is taken whole ends early.
-//      If more keys equal the threshold key T than are still needed, the same
-//      passes run over the block id (lowest first) among keys == T, so ties go
-//      to the lower block id.  (If the candidates overflow LDS, the passes run
-//      over the register-resident row instead; the result is the same.)
-//   4. the k winners are gathered into LDS and bitonic-sorted into rank order
-//      (key desc, id asc): in registers with wave shuffles for strides < 64,
-//      through LDS above that.
+//   3. if at most 1024 keys are candidates (the usual case), they are sorted
+//      whole (step 4) and the first k kept.  Otherwise a radix select on the
+//      candidates: up to four MSB-first passes over 8-bit digits, each a
+//      256-bin LDS histogram (one sub-histogram per wave), a suffix scan to
+//      find the bin holding the k-th largest key, and the prefix grows by that
+//      digit; a pass whose bin is taken whole ends early.  If more keys equal
+//      the threshold key T than are still needed, the same passes run over the
+//      block id (lowest first) among keys == T, so ties go to the lower block
+//      id.  (If the candidates overflow LDS, the passes run over the
+//      register-resident row instead; the result is the same.)
+//   4. bitonic sort into rank order (key desc, id asc): in registers with lane
+//      exchanges for strides < 64, through LDS above that.
 #include <hip/hip_runtime.h>
 
 #include "qsa_device.h"
@@ -41,6 +42,7 @@ constexpr int MAXK = kTopkMaxK;
 constexpr int CAP = 8192;  // LDS candidate capacity
 
 struct TopkShared {
+  uint64_t wbuf[NT];           // rank words of the sort's cross-wave steps
   uint32_t hsub[NWAVES][256];  // per-wave digit histograms
   uint32_t wtot[4];            // scan carry of the four scanning waves
   uint32_t bcast[3];           // chosen digit, remaining k, count in the bin
@@ -177,73 +179,72 @@ __device__ __forceinline__ void compact(Visit &&visit, Pred &&pred, uint32_t *co
   });
 }
 
-// Rank-order sort of sh.bkey/bid[0, m) and the store of one row of ids.
-__device__ void sort_and_store(TopkShared &sh, int m, int k, int *__restrict__ orow) {
+// Rank-order sort of the n (key, id) pairs in LDS arrays skey/sid (which the
+// large-P path also uses as scratch), then the store of one row of ids: the
+// first m in rank order, then -1 up to k.  `wbuf` is NT words of LDS scratch.
+// Every thread of the workgroup must call it.
+__device__ void sort_and_store(uint32_t *skey, uint32_t *sid, int n, int m, int k,
+                               int *__restrict__ orow, uint64_t *wbuf) {
   const int t = threadIdx.x;
   int P = 1;
-  while (P < m) P <<= 1;
+  while (P < n) P <<= 1;
   if (P <= NT) {
-    // One element per thread: strides below 64 exchange inside the wave,
-    // larger strides through LDS.
-    uint32_t key = 0u, id = 0xFFFFFFFFu;  // padding ranks after every winner
-    if (t < m) {
-      key = sh.bkey[t];
-      id = sh.bid[t];
-    }
-    auto rank_before = [](uint32_t ka, uint32_t ia, uint32_t kb, uint32_t ib) {
-      return (ka > kb) | ((ka == kb) & (ia < ib));
-    };
+    // One rank word per thread (padding: word 0, after every element).
+    // Strides below 64 exchange inside the wave, larger strides through LDS.
+    // Waves past the P elements only keep the barriers.
+    const bool busy = (t & ~63) < P;  // wave-uniform
+    uint64_t w = t < n ? rank_word(skey[t], sid[t]) : 0ull;
     auto lds_step = [&](int size, int stride) {
       __syncthreads();
-      sh.bkey[t] = key;
-      sh.bid[t] = id;
+      if (busy) wbuf[t] = w;
       __syncthreads();
-      const uint32_t pk = sh.bkey[t ^ stride], pi = sh.bid[t ^ stride];
-      const bool take_first = ((t & stride) == 0) == ((t & size) == 0);
-      const bool take =
-          (take_first & rank_before(pk, pi, key, id)) | (!take_first & rank_before(key, id, pk, pi));
-      key = take ? pk : key;
-      id = take ? pi : id;
+      if (busy) {
+        const uint64_t p = wbuf[t ^ stride];
+        const bool keep_larger = ((t & stride) == 0) == ((t & size) == 0);
+        w = ((p > w) == keep_larger) ? p : w;
+      }
     };
     // Stages 2..64 run whole inside each wave; later stages start with their
     // cross-wave strides, then finish with the in-wave ones.
-    if (P >= 2) bitonic_lane_stage<2, 1>(key, id, t, rank_before);
-    if (P >= 4) bitonic_lane_stage<4, 2>(key, id, t, rank_before);
-    if (P >= 8) bitonic_lane_stage<8, 4>(key, id, t, rank_before);
-    if (P >= 16) bitonic_lane_stage<16, 8>(key, id, t, rank_before);
-    if (P >= 32) bitonic_lane_stage<32, 16>(key, id, t, rank_before);
-    if (P >= 64) bitonic_lane_stage<64, 32>(key, id, t, rank_before);
+    if (busy) {
+      if (P >= 2) bitonic_word_stage<2, 1>(w, t);
+      if (P >= 4) bitonic_word_stage<4, 2>(w, t);
+      if (P >= 8) bitonic_word_stage<8, 4>(w, t);
+      if (P >= 16) bitonic_word_stage<16, 8>(w, t);
+      if (P >= 32) bitonic_word_stage<32, 16>(w, t);
+      if (P >= 64) bitonic_word_stage<64, 32>(w, t);
+    }
     if (P >= 128) {
       lds_step(128, 64);
-      bitonic_lane_stage<128, 32>(key, id, t, rank_before);
+      if (busy) bitonic_word_stage<128, 32>(w, t);
     }
     if (P >= 256) {
       lds_step(256, 128);
       lds_step(256, 64);
-      bitonic_lane_stage<256, 32>(key, id, t, rank_before);
+      if (busy) bitonic_word_stage<256, 32>(w, t);
     }
     if (P >= 512) {
       lds_step(512, 256);
       lds_step(512, 128);
       lds_step(512, 64);
-      bitonic_lane_stage<512, 32>(key, id, t, rank_before);
+      if (busy) bitonic_word_stage<512, 32>(w, t);
     }
     if (P >= 1024) {
       lds_step(1024, 512);
       lds_step(1024, 256);
       lds_step(1024, 128);
       lds_step(1024, 64);
-      bitonic_lane_stage<1024, 32>(key, id, t, rank_before);
+      bitonic_word_stage<1024, 32>(w, t);
     }
-    if (t < m) orow[t] = int(id);
+    if (t < m) orow[t] = int(~uint32_t(w));
     for (int r = m + t; r < k; r += NT) orow[r] = -1;
     return;
   }
   // P in (NT, MAXK]: bitonic network over LDS.
   __syncthreads();
-  for (int i = m + t; i < P; i += NT) {
-    sh.bkey[i] = 0u;
-    sh.bid[i] = 0xFFFFFFFFu;
+  for (int i = n + t; i < P; i += NT) {
+    skey[i] = 0u;
+    sid[i] = 0xFFFFFFFFu;
   }
   __syncthreads();
   for (int size = 2; size <= P; size <<= 1) {
@@ -251,21 +252,21 @@ __device__ void sort_and_store(TopkShared &sh, int m, int k, int *__restrict__ o
       for (int p = t; p < (P >> 1); p += NT) {
         const int i = ((p & ~(stride - 1)) << 1) | (p & (stride - 1));
         const int j = i + stride;
-        const uint32_t ki = sh.bkey[i], kj = sh.bkey[j];
-        const uint32_t ii = sh.bid[i], ij = sh.bid[j];
+        const uint32_t ki = skey[i], kj = skey[j];
+        const uint32_t ii = sid[i], ij = sid[j];
         const bool j_first = kj > ki || (kj == ki && ij < ii);
         const bool forward = (i & size) == 0;
         if (j_first == forward) {
-          sh.bkey[i] = kj;
-          sh.bkey[j] = ki;
-          sh.bid[i] = ij;
-          sh.bid[j] = ii;
+          skey[i] = kj;
+          skey[j] = ki;
+          sid[i] = ij;
+          sid[j] = ii;
         }
       }
       __syncthreads();
     }
   }
-  for (int r = t; r < k; r += NT) orow[r] = r < m ? int(sh.bid[r]) : -1;
+  for (int r = t; r < k; r += NT) orow[r] = r < m ? int(sid[r]) : -1;
 }
 
 template <int PER>
@@ -391,6 +392,12 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
   __syncthreads();
   const uint32_t C = sh.ncand;
 
+  if (C <= uint32_t(NT)) {
+    // Few candidates (the usual case): sort them all into rank order and
+    // keep the first m -- every winner is a candidate.
+    sort_and_store(sh.ckey, sh.cid, int(C), m, k, orow, sh.wbuf);
+    return;
+  }
   if (C <= uint32_t(CAP)) {
     // Select among the LDS candidates (all of them when k >= C).
     const uint32_t padC = (C + NT - 1) / NT * NT;
@@ -411,7 +418,7 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
             &sh.nwin, sh.bkey, sh.bid, MAXK);
   }
   __syncthreads();
-  sort_and_store(sh, m, k, orow);
+  sort_and_store(sh.bkey, sh.bid, m, m, k, orow, sh.wbuf);
 }
 
 template <int PER>
