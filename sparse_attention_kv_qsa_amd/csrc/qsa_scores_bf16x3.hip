@@ -98,6 +98,14 @@ __device__ __forceinline__ f16v mfma_bf16(u4 a, u4 b, f16v c) {
                                                  __builtin_bit_cast(bf8, b), c, 0, 0, 0);
 }
 
+// LDS slots of a step's block planes are [ks][column half][lane]; lane l of
+// K group g = 2 ks + l/32 sits at l ^ lane_swz(g).  Without the swizzle the
+// four K groups a thread quartet writes (one block row) fall on the same
+// banks; with it, both the writes (8 or 16 lanes per pass) and the MFMA-lane
+// reads (a permutation of consecutive slots) are free of bank conflicts for
+// 32 or 64 four-byte banks.
+__device__ __forceinline__ int lane_swz(int g) { return (g << 2) ^ ((g >> 1) << 1); }
+
 // One 128 x 64 tile.  FULL: all 64 block rows active; otherwise a 32-block
 // half without an active block skips its MFMAs.
 template <bool FULL>
@@ -122,7 +130,7 @@ __device__ __forceinline__ void split_tile(const float *__restrict__ q,
   const int brow = t >> 2;
   const int bkg = t & 3;
   const uint32_t boff = uint32_t(brow) * row_bytes;
-  const int bslot = ((bkg >> 1) * 2 + (brow >> 5)) * 64 + (brow & 31) + 32 * (bkg & 1);
+  const int bslot = ((bkg >> 1) * 2 + (brow >> 5)) * 64 + (((brow & 31) + 32 * (bkg & 1)) ^ lane_swz(bkg));
   constexpr int kPlane = 2 * 2 * 64;  // u4 entries per plane of one step
 
   auto eoff = [&](int e) -> uint32_t { return e < K ? uint32_t(e) * 4u : kOutOfRange; };
@@ -177,7 +185,7 @@ __device__ __forceinline__ void split_tile(const float *__restrict__ q,
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) {
         if (FULL || ni < nni) {
-          const int o = (ks * 2 + ni) * 64 + lane;
+          const int o = (ks * 2 + ni) * 64 + (lane ^ lane_swz(2 * ks + h));
           pbv[ks][ni].hi = cur[0 * kPlane + o];
           pbv[ks][ni].mid = cur[1 * kPlane + o];
           pbv[ks][ni].lo = cur[2 * kPlane + o];
