@@ -68,7 +68,7 @@ def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default=synth.HEADLINE, choices=list(synth.WORKLOADS))
     p.add_argument("--copies", type=int, default=6,
                    help="input copies rotated over the steps (defeats cache reuse)")
