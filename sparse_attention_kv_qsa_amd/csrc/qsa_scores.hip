@@ -106,8 +106,11 @@ __global__ __launch_bounds__(256) void scores_gemv_kernel(const float *__restric
 // n's M best rank words of the group -- what the top-k's first kernel would
 // compute from the stored scores, without reading them back.
 // ---------------------------------------------------------------------------
+// Two 16-wave workgroups per CU when the registers allow (8 waves per SIMD,
+// at most 64 VGPRs): one workgroup per CU would leave the CU idle through
+// each workgroup's barrier and sort.
 template <int NQ, int NC, int U>
-__global__ __launch_bounds__(1024) void scores_gemv_tops_kernel(const float *__restrict__ q,
+__global__ __launch_bounds__(1024, ((NQ + U) * NC <= 10 ? 8 : 4)) void scores_gemv_tops_kernel(const float *__restrict__ q,
                                                                 const float *__restrict__ kblk,
                                                                 int nq, int K, int A,
                                                                 float *__restrict__ scores,
@@ -169,7 +172,9 @@ __global__ __launch_bounds__(1024) void scores_gemv_tops_kernel(const float *__r
 template <int NQ, int NC>
 hipError_t launch_gemv_tops_nc(const float *q, const float *kblk, int nq, int K, int A,
                                float *scores, uint64_t *tops, int M, hipStream_t stream) {
-  constexpr int U = NC >= 8 ? 1 : NC >= 4 ? 2 : 4;
+  // rows per batch: the loaded summaries (U x NC float4s) and the queries
+  // (NQ x NC) together stay near 16 float4s per lane
+  constexpr int U = NQ * NC >= 8 ? 1 : NQ * NC >= 4 ? 2 : 4;
   const int ngroups = (A + 63) / 64;
   scores_gemv_tops_kernel<NQ, NC, U><<<ngroups, 1024, 0, stream>>>(q, kblk, nq, K, A, scores, tops,
                                                                  ngroups, M);

@@ -61,7 +61,10 @@ class Workload:
 
 
 # The five workloads: a tiny decode call, 32K and 128K prompts, a 128K decode
-# call inside a 262,144-cell capacity, and a 256K near-tie prompt stress case.
+# call inside a 262,144-cell capacity, and a 256K near-tie prompt stress case;
+# then multi-query decode at 128K (2 and 4 queries per call, the T = 2 and
+# T = 4 rows of the decode table of "#3108 perf(hip): ...": speculative
+# verification scores several queries against the same summaries).
 WORKLOADS = {
     w.name: w
     for w in [
@@ -74,6 +77,10 @@ WORKLOADS = {
                  k=512, needle_frac=0.01, poison=True),
         Workload("prompt-256k-tie", nq=256, heads=4, dim=128, active=65538,
                  capacity=65538, k=1024, needle_frac=0.001, tie_vectors=64),
+        Workload("decode-128k-t2", nq=2, heads=4, dim=128, active=32770, capacity=65538,
+                 k=512, poison=True),
+        Workload("decode-128k-t4", nq=4, heads=4, dim=128, active=32770, capacity=65538,
+                 k=512, poison=True),
     ]
 }
 

@@ -10,7 +10,9 @@ from sparse_attention_kv_qsa_amd import synth
 def test_workload_table():
     w = synth.WORKLOADS
     assert [x.name for x in w.values()] == ["tiny-decode", "prompt-32k", "decode-128k",
-                                            "prompt-128k", "prompt-256k-tie"]
+                                            "prompt-128k", "prompt-256k-tie",
+                                            "decode-128k-t2", "decode-128k-t4"]
+    assert [w[n].nq for n in ("decode-128k", "decode-128k-t2", "decode-128k-t4")] == [1, 2, 4]
     assert (w["tiny-decode"].active, w["tiny-decode"].K, w["tiny-decode"].k) == (512, 256, 64)
     assert (w["prompt-32k"].nq, w["prompt-32k"].active, w["prompt-32k"].k) == (256, 8193, 256)
     assert (w["decode-128k"].active, w["decode-128k"].capacity) == (32770, 65538)
