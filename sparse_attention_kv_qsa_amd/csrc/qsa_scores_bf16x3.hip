@@ -49,6 +49,7 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 constexpr int BM = 128;  // queries per tile
 constexpr int BN = 64;   // blocks per tile
 constexpr int BK = 32;   // K elements per step
+constexpr int BT = 64;   // queries per narrow ragged tile (split_tail)
 constexpr uint32_t kOutOfRange = 0x40000000u;  // byte offset past any tile resource
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const float *base, uint32_t bytes) {
@@ -238,20 +239,122 @@ __device__ __forceinline__ void split_tile(const float *__restrict__ q,
   }
 }
 
+// A ragged tile whose active blocks fit one 32-block column half (A % 64 in
+// 1..32), for 64 queries.  The two K halves of every step are independent
+// accumulations until the final sum (hh_0, c_0 and hh_1, c_1 above), so wave
+// w takes query group w / 2 and K half w % 2 only: each wave runs half the
+// MFMAs and half the query split of a full-width ragged tile, and the tail
+// spreads over twice as many workgroups.  Each accumulator receives the same
+// MFMAs in the same order as in split_tile, and the halves meet in LDS in the
+// same expression, so the scores are bitwise those of a full tile.
+__device__ __forceinline__ void split_tail(const float *__restrict__ q,
+                                           const float *__restrict__ kblk, int nq, int K, int A,
+                                           float *__restrict__ scores, int q0, int b0, u4 *bl) {
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int qg = wave >> 1;  // query group: rows q0 + 32 qg ..
+  const int kh = wave & 1;   // K half of every step
+  const int r32 = lane & 31;
+  const int h = lane >> 5;
+
+  const uint32_t row_bytes = uint32_t(K) * 4u;
+  const __amdgpu_buffer_rsrc_t rq = tile_rsrc(q + int64_t(q0) * K, uint32_t(min(BT, nq - q0)) * row_bytes);
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kblk + int64_t(b0) * K, uint32_t(min(BN, A - b0)) * row_bytes);
+  const uint32_t qrow = uint32_t(32 * qg + r32) * row_bytes;
+  const int brow = t >> 2;
+  const int bkg = t & 3;
+  const uint32_t boff = uint32_t(brow) * row_bytes;
+  const int bslot = ((bkg >> 1) * 2 + (brow >> 5)) * 64 + (((brow & 31) + 32 * (bkg & 1)) ^ lane_swz(bkg));
+  constexpr int kPlane = 2 * 2 * 64;
+  auto eoff = [&](int e) -> uint32_t { return e < K ? uint32_t(e) * 4u : kOutOfRange; };
+
+  f16v hh = f16v{}, cc = f16v{};
+  f4 qa[2], kb[2];
+  auto load = [&](int kk) {
+    qa[0] = buffer_f4(rq, qrow + eoff(kk + 16 * kh + 8 * h));
+    qa[1] = buffer_f4(rq, qrow + eoff(kk + 16 * kh + 8 * h + 4));
+    kb[0] = buffer_f4(rk, boff + eoff(kk + 8 * bkg));
+    kb[1] = buffer_f4(rk, boff + eoff(kk + 8 * bkg + 4));
+  };
+  auto publish = [&](u4 *buf) {
+    const Planes pb = split8(kb[0], kb[1]);
+    buf[0 * kPlane + bslot] = pb.hi;
+    buf[1 * kPlane + bslot] = pb.mid;
+    buf[2 * kPlane + bslot] = pb.lo;
+  };
+  const int nsteps = (K + BK - 1) / BK;
+  auto step = [&](int s, const Planes &use, Planes &fill) {
+    const u4 *cur = bl + (s & 1) * (3 * kPlane);
+    u4 *nxt = bl + ((s + 1) & 1) * (3 * kPlane);
+    fill = split8(qa[0], qa[1]);
+    publish(nxt);
+    load((s + 2) * BK);
+    __builtin_amdgcn_sched_barrier(0);
+    const int o = (kh * 2) * 64 + (lane ^ lane_swz(2 * kh + h));
+    Planes y;
+    y.hi = cur[0 * kPlane + o];
+    y.mid = cur[1 * kPlane + o];
+    y.lo = cur[2 * kPlane + o];
+    hh = mfma_bf16(use.hi, y.hi, hh);
+    cc = mfma_bf16(use.hi, y.mid, cc);
+    cc = mfma_bf16(use.mid, y.hi, cc);
+    cc = mfma_bf16(use.hi, y.lo, cc);
+    cc = mfma_bf16(use.mid, y.mid, cc);
+    cc = mfma_bf16(use.lo, y.hi, cc);
+    __syncthreads();
+  };
+  Planes pa, pn;
+  load(0);
+  pa = split8(qa[0], qa[1]);
+  publish(bl);
+  load(BK);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, pa, pn);
+    if (s + 1 < nsteps) step(s + 1, pn, pa);
+  }
+  // The K-half-1 waves hand their accumulators over through LDS (free after
+  // the last step's barrier): [query group][register][lane].
+  float *xch = reinterpret_cast<float *>(bl);
+  if (kh == 1) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      xch[(qg * 32 + r) * 64 + lane] = hh[r];
+      xch[(qg * 32 + 16 + r) * 64 + lane] = cc[r];
+    }
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const int col = b0 + r32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float v = (hh[r] + xch[(qg * 32 + r) * 64 + lane]) + (cc[r] + xch[(qg * 32 + 16 + r) * 64 + lane]);
+      const int row = q0 + 32 * qg + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row < nq && col < A) scores[int64_t(row) * A + col] = v;
+    }
+  }
+}
+
 // Tile assignment as in the fp32 scorer: workgroup ids go round-robin over
 // the 8 XCDs; each XCD takes an equal share of the full tiles (query tiles
-// of one block tile adjacent) and every eighth ragged tile, ragged first.
+// of one block tile adjacent) and every eighth ragged unit, ragged first.  A
+// ragged unit is a 64-query split_tail tile when the ragged column has at
+// most 32 active blocks (narrow), else a 128-query split_tile<false> tile.
 __global__ __launch_bounds__(256, 2) void scores_bf16x3_kernel(const float *__restrict__ q,
                                                                const float *__restrict__ kblk,
                                                                int nq, int K, int A,
                                                                float *__restrict__ scores,
-                                                               int nqt, int nct, int ntail) {
+                                                               int nqt, int nct, int ntail,
+                                                               int narrow) {
   __shared__ u4 bl[2 * 3 * 2 * 2 * 64];  // 24 KB: two steps x three planes x (2 K halves x 2 column halves x 64 lanes)
   const int x = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int tails_here = ntail > x ? (ntail - x + 7) / 8 : 0;
   if (slot < tails_here) {
-    split_tile<false>(q, kblk, nq, K, A, scores, (x + 8 * slot) * BM, (nct - 1) * BN, bl);
+    const int u = x + 8 * slot;  // ragged unit
+    if (narrow) split_tail(q, kblk, nq, K, A, scores, u * BT, (nct - 1) * BN, bl);
+    else split_tile<false>(q, kblk, nq, K, A, scores, u * BM, (nct - 1) * BN, bl);
     return;
   }
   const int64_t nfull = int64_t(nqt) * (nct - (ntail > 0 ? 1 : 0));
@@ -266,7 +369,9 @@ hipError_t launch_block_scores_bf16x3(const float *q, const float *kblk, int nq,
                                       float *scores, hipStream_t stream) {
   const int nqt = (nq + BM - 1) / BM;
   const int nct = (A + BN - 1) / BN;
-  const int ntail = (A % BN) ? nqt : 0;
+  const int rag = A % BN;
+  const int narrow = rag > 0 && rag <= 32;
+  const int ntail = rag == 0 ? 0 : narrow ? (nq + BT - 1) / BT : nqt;
   const int64_t nfull = int64_t(nqt) * (nct - (ntail ? 1 : 0));
   int64_t per = 0;  // workgroups per XCD: the largest share
   for (int x = 0; x < 8; ++x) {
@@ -274,7 +379,7 @@ hipError_t launch_block_scores_bf16x3(const float *q, const float *kblk, int nq,
     per = std::max(per, tails + nfull * (x + 1) / 8 - nfull * x / 8);
   }
   scores_bf16x3_kernel<<<int(8 * per), 256, 0, stream>>>(q, kblk, nq, K, A, scores, nqt, nct,
-                                                         ntail);
+                                                         ntail, narrow);
   return hipGetLastError();
 }
 

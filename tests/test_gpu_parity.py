@@ -142,12 +142,14 @@ def test_scores_within_gate(nq, heads, dim, active, mode):
 @pytest.mark.parametrize("mode", MODES)
 def test_scores_deterministic_and_position_invariant(mode):
     rng = np.random.default_rng(12)
-    for nq in (1, 5, 100, 300):
+    # 700 blocks end in a 60-block ragged column, 705 in a 1-block one (the
+    # split-K ragged path of the bf16 scorer)
+    for nq, a in ((1, 700), (5, 705), (100, 700), (300, 700), (300, 705), (70, 705)):
         vec = rng.standard_normal((4, 4, 128)).astype(np.float32)
-        assign = rng.integers(0, 4, 700)
+        assign = rng.integers(0, 4, a)
         kb = np.ascontiguousarray(vec[assign])
         q = rng.standard_normal((nq, 4, 128)).astype(np.float32)
-        s1, s2 = gpu_scores(q, kb, 700, mode), gpu_scores(q, kb, 700, mode)
+        s1, s2 = gpu_scores(q, kb, a, mode), gpu_scores(q, kb, a, mode)
         assert np.array_equal(s1, s2)
         for c in range(4):
             cols = s1[:, assign == c]
