@@ -23,7 +23,10 @@
 // consecutive elements of block row t/4, splits them and writes the three
 // 16-byte planes to LDS exactly where the MFMA lane that needs them will read
 // them; two LDS buffers alternate, one barrier per step.  Each wave splits its
-// own query slices in registers.  A wave keeps eight accumulators per tile
+// own query slices in registers.  When K is a multiple of 32 the wave's query
+// rows reach it through LDS: direct buffer-to-LDS loads in which 8 lanes read
+// one 128-byte row segment (a load instruction touches 8 cache lines instead
+// of 32), then one ds_read per MFMA slice.  A wave keeps eight accumulators per tile
 // column half: hi*hi and corrections, each separately for the two K halves
 // of a step (so that no accumulator is reused within four MFMAs); the score
 // is (hh_0 + hh_1) + (c_0 + c_1).  No cross-wave combine: each wave stores
@@ -31,7 +34,9 @@
 //
 // Position invariance: a ragged tile runs the same per-element instruction
 // sequence (hardware-bounded buffer loads return zeros past the valid rows;
-// zero slices add exact zeros), so equal summaries score bitwise-equal.
+// zero slices add exact zeros), so equal summaries score bitwise-equal.  A
+// ragged column of at most 32 blocks is split by K half (split_tail) without
+// changing any accumulator's sequence of MFMAs.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -109,10 +114,13 @@ __device__ __forceinline__ int lane_swz(int g) { return (g << 2) ^ ((g >> 1) << 
 
 // One 128 x 64 tile.  FULL: all 64 block rows active; otherwise a 32-block
 // half without an active block skips its MFMAs.
-template <bool FULL>
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <bool FULL, bool QD>
 __device__ __forceinline__ void split_tile(const float *__restrict__ q,
                                            const float *__restrict__ kblk, int nq, int K, int A,
-                                           float *__restrict__ scores, int q0, int b0, u4 *bl) {
+                                           float *__restrict__ scores, int q0, int b0, u4 *bl,
+                                           u4 *qst) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -146,11 +154,40 @@ __device__ __forceinline__ void split_tile(const float *__restrict__ q,
       for (int ni = 0; ni < 2; ++ni) acc[a][c][ni] = f16v{};
 
   f4 qa[2][2], kb[2];
-  auto load = [&](int kk) {
+  // QD (K a multiple of 32): the wave's 32 query rows of a step go global ->
+  // LDS by direct loads, 8 lanes per 128-byte row segment, piece p of row r
+  // at slot p ^ ((r >> 1) & 7); the lanes then read their MFMA slices.
+  uint32_t dq[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      qa[ks][0] = buffer_f4(rq, qrow + eoff(kk + 16 * ks + 8 * h));
-      qa[ks][1] = buffer_f4(rq, qrow + eoff(kk + 16 * ks + 8 * h + 4));
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    const int p = (lane & 7) ^ ((r >> 1) & 7);
+    dq[i] = uint32_t(32 * wave + r) * row_bytes + uint32_t(p) * 16u;
+  }
+  auto dma_q = [&](int buf, int kk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(qst + buf * 256 + i * 64), 16, dq[i],
+                                               kk * 4, 0, 0);
+  };
+  auto read_q = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int p = 4 * ks + 2 * h + half;
+        qa[ks][half] = __builtin_bit_cast(f4, qst[buf * 256 + r32 * 8 + (p ^ ((r32 >> 1) & 7))]);
+      }
+  };
+  auto load = [&](int kk) {
+    if (QD) {
+      if (kk < K) dma_q((kk / BK) & 1, kk);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        qa[ks][0] = buffer_f4(rq, qrow + eoff(kk + 16 * ks + 8 * h));
+        qa[ks][1] = buffer_f4(rq, qrow + eoff(kk + 16 * ks + 8 * h + 4));
+      }
     }
     kb[0] = buffer_f4(rk, boff + eoff(kk + 8 * bkg));
     kb[1] = buffer_f4(rk, boff + eoff(kk + 8 * bkg + 4));
@@ -166,7 +203,10 @@ __device__ __forceinline__ void split_tile(const float *__restrict__ q,
   // splits the raw data of step s + 1 (its query slices into registers, its
   // share of the block slices into the other LDS buffer) and at once issues
   // the loads of step s + 2, so they have the whole MFMA section of step s to
-  // arrive; a scheduling barrier keeps the compiler from sinking them.  One
+  // arrive; a scheduling barrier keeps the compiler from sinking them.  With
+  // QD the query rows of step s + 2 land in the wave's other staging buffer
+  // (the workgroup barrier at the end of step s waits for them, as for any
+  // LDS write).  One
   // workgroup barrier per step publishes the next buffer and retires the
   // reads of the buffer it will overwrite.  The loop is unrolled by two so
   // the query planes of consecutive steps alternate between two register
@@ -175,9 +215,14 @@ __device__ __forceinline__ void split_tile(const float *__restrict__ q,
   auto step = [&](int s, const Planes (&use)[2], Planes (&fill)[2]) {
     const u4 *cur = bl + (s & 1) * (3 * kPlane);
     u4 *nxt = bl + ((s + 1) & 1) * (3 * kPlane);
+    if (QD) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this step's staged queries and blocks
+      read_q((s + 1) & 1);
+      publish(nxt);
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) fill[ks] = split8(qa[ks][0], qa[ks][1]);
-    publish(nxt);
+    if (!QD) publish(nxt);
     load((s + 2) * BK);  // past K: out-of-range offsets, no memory access
     __builtin_amdgcn_sched_barrier(0);
     Planes pbv[2][2];  // [ks][ni]
@@ -217,6 +262,10 @@ __device__ __forceinline__ void split_tile(const float *__restrict__ q,
 
   Planes pa[2], pn[2];
   load(0);
+  if (QD) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    read_q(0);
+  }
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) pa[ks] = split8(qa[ks][0], qa[ks][1]);
   publish(bl);
@@ -348,19 +397,22 @@ __global__ __launch_bounds__(256, 2) void scores_bf16x3_kernel(const float *__re
                                                                int nqt, int nct, int ntail,
                                                                int narrow) {
   __shared__ u4 bl[2 * 3 * 2 * 2 * 64];  // 24 KB: two steps x three planes x (2 K halves x 2 column halves x 64 lanes)
+  __shared__ u4 qst[4 * 2 * 256];       // 32 KB: per wave, two steps of 32 query rows x 128 bytes
   const int x = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int tails_here = ntail > x ? (ntail - x + 7) / 8 : 0;
   if (slot < tails_here) {
     const int u = x + 8 * slot;  // ragged unit
     if (narrow) split_tail(q, kblk, nq, K, A, scores, u * BT, (nct - 1) * BN, bl);
-    else split_tile<false>(q, kblk, nq, K, A, scores, u * BM, (nct - 1) * BN, bl);
+    else split_tile<false, false>(q, kblk, nq, K, A, scores, u * BM, (nct - 1) * BN, bl, qst);
     return;
   }
   const int64_t nfull = int64_t(nqt) * (nct - (ntail > 0 ? 1 : 0));
   const int64_t f = nfull * x / 8 + (slot - tails_here);
   if (f >= nfull * (x + 1) / 8) return;  // whole workgroup leaves before any barrier
-  split_tile<true>(q, kblk, nq, K, A, scores, int(f % nqt) * BM, int(f / nqt) * BN, bl);
+  u4 *mq = qst + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 512;
+  if (K % BK == 0) split_tile<true, true>(q, kblk, nq, K, A, scores, int(f % nqt) * BM, int(f / nqt) * BN, bl, mq);
+  else split_tile<true, false>(q, kblk, nq, K, A, scores, int(f % nqt) * BM, int(f / nqt) * BN, bl, mq);
 }
 
 }  // namespace
