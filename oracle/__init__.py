@@ -16,6 +16,10 @@ select - WMMA block scorer, prompt-aware top-k dispatch", What items 1-2):
 * ``topk(scores, k)``: for each row, the ids of the k largest scores, ties to
   the lower id, in rank order; slots past the row length hold -1.
 * ``topk_f64(scores64, k)``: the same order on FP64 scores (diagnostic only).
+* ``sparse_decode_attn_f64(q, kc, vc, ids, n_cells, scale)``: FP64 decode
+  attention of each query and head over the cells of its listed blocks (page
+  "#3102 perf(hip): enable wave32 QSA decode attention and MMVQ row reuse on
+  gfx12", Summary item 1).
 
 Every function here is pinned by tests/test_oracle.py (hand example, exact
 integer inputs, exact rationals, numpy float64 matmul, brute-force rank,
@@ -72,6 +76,9 @@ def _bind(path: str):
     lib.oracle_block_topk.restype = ctypes.c_int
     lib.oracle_block_topk_f64.argtypes = [vp, i64, i64, i64, vp]
     lib.oracle_block_topk_f64.restype = ctypes.c_int
+    lib.oracle_sparse_decode_attn_f64.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                                  ctypes.c_double, vp]
+    lib.oracle_sparse_decode_attn_f64.restype = ctypes.c_int
     return lib
 
 
@@ -131,6 +138,25 @@ class Oracle:
         _check(self.lib.oracle_block_topk_f64(_ptr(scores), nq, a, k, _ptr(ids)))
         return ids
 
+    def sparse_decode_attn_f64(self, q: np.ndarray, kc: np.ndarray, vc: np.ndarray,
+                               ids: np.ndarray, n_cells: int, scale: float) -> np.ndarray:
+        """FP64 attention of q[nq][heads][dim] over the cells of the blocks ids[nq][k]
+        (-1 skipped) in kc/vc[cells][heads][dim], cells c < n_cells only."""
+        q = np.ascontiguousarray(q, dtype=np.float32)
+        kc = np.ascontiguousarray(kc, dtype=np.float32)
+        vc = np.ascontiguousarray(vc, dtype=np.float32)
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        nq, heads, dim = q.shape
+        if ids.ndim != 2 or ids.shape[0] != nq:
+            raise ValueError("ids must be [nq][k]")
+        if kc.shape[1:] != (heads, dim) or vc.shape != kc.shape or kc.shape[0] < n_cells:
+            raise ValueError("kc and vc must be [>=n_cells][heads][dim]")
+        out = np.empty((nq, heads, dim), dtype=np.float64)
+        _check(self.lib.oracle_sparse_decode_attn_f64(_ptr(q), _ptr(kc), _ptr(vc), _ptr(ids), nq,
+                                                      heads, dim, ids.shape[1], n_cells,
+                                                      float(scale), _ptr(out)))
+        return out
+
 
 def default() -> Oracle:
     return Oracle(_load())
@@ -151,3 +177,7 @@ def topk(scores, k):
 
 def topk_f64(scores, k):
     return default().topk_f64(scores, k)
+
+
+def sparse_decode_attn_f64(q, kc, vc, ids, n_cells, scale):
+    return default().sparse_decode_attn_f64(q, kc, vc, ids, n_cells, scale)

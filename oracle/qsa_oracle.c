@@ -10,6 +10,11 @@
  * Built with plain gcc (-O2, no -ffast-math, no FTZ); see oracle/__init__.py.
  *
  * Sources (web pages on the selection path of a closed inference engine):
+ *   [P3] "#3102 perf(hip): enable wave32 QSA decode attention and MMVQ row
+ *        reuse on gfx12", Summary item 1 (decode attention over the cells of
+ *        the selected blocks, computed in chunks whose partial results are
+ *        merged in sequential chunk order) and the decode-attention
+ *        microbenchmark table (attended widths, one or four queries).
  *   [P1] "#3108 perf(hip): optimize exact QSA block scoring and top-k selection
  *        on gfx12", Summary item 1 (a block score is the sum over the query's
  *        heads of per-head dot products against the block's key summary) and
@@ -27,7 +32,11 @@
  *   - ties in score go to the lower block id; -0.0 and +0.0 are equal;
  *   - ids come out in rank order (score descending, id ascending), and slots
  *     past active_blocks (k > active_blocks) hold -1;
- *   - scores must be finite (NaN is reported as an error).
+ *   - scores must be finite (NaN is reported as an error);
+ *   - decode attention ([P3]): per query and head, scaled dot-product
+ *     attention over the cells of the listed blocks (block b holds cells
+ *     4b .. 4b+3; cells at or past n_cells and ids of -1 are skipped), with a
+ *     caller-given scale; no attended cell gives a zero output.
  *
  * Pins (what this oracle is checked against, not itself): a hand-worked
  * 3-block example, exact integer inputs vs numpy int64 matmul, exact rationals
@@ -159,5 +168,66 @@ int oracle_block_topk_f64(const double *scores, int64_t nq, int64_t active_block
     topk_row(c, active_blocks, k, ids + i * k);
   }
   free(c);
+  return ORACLE_OK;
+}
+
+/*
+ * Block-sparse decode attention in FP64 ([P3] Summary item 1): for query i
+ * and head h, over the attended cells c (the cells 4b .. 4b+3 of every listed
+ * block b = ids[i][j] >= 0, j < k, with c < n_cells; a block listed twice
+ * counts twice),
+ *   s_c = scale * sum_{d<dim} q[i][h][d] * kc[c][h][d]
+ *   w_c = exp(s_c - max_c s_c)
+ *   out[i][h][d] = sum_c w_c * vc[c][h][d] / sum_c w_c
+ * and out = 0 when no cell is attended.  Layouts: q[nq][heads][dim],
+ * kc and vc [cells][heads][dim], ids[nq][k], out[nq][heads][dim].
+ * The cells are visited in list order, the four cells of a block in order.
+ */
+int oracle_sparse_decode_attn_f64(const float *q, const float *kc, const float *vc,
+                                  const int32_t *ids, int64_t nq, int64_t heads,
+                                  int64_t dim, int64_t k, int64_t n_cells, double scale,
+                                  double *out) {
+  if (nq < 0 || heads < 0 || dim < 0 || k < 0 || n_cells < 0) return ORACLE_ERR_ARG;
+  if (nq == 0 || heads == 0 || dim == 0) return ORACLE_OK;
+  if (!q || !out || (k > 0 && (!ids || !kc || !vc))) return ORACLE_ERR_ARG;
+  double *s = (double *)malloc(sizeof(double) * (size_t)(4 * k > 0 ? 4 * k : 1));
+  int64_t *cell = (int64_t *)malloc(sizeof(int64_t) * (size_t)(4 * k > 0 ? 4 * k : 1));
+  if (!s || !cell) {
+    free(s);
+    free(cell);
+    return ORACLE_ERR_NOMEM;
+  }
+  for (int64_t i = 0; i < nq; ++i) {
+    /* the attended cells of this query, in list order */
+    int64_t n = 0;
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t b = ids[i * k + j];
+      if (b < 0) continue;
+      for (int64_t e = 0; e < 4; ++e)
+        if (4 * b + e < n_cells) cell[n++] = 4 * b + e;
+    }
+    for (int64_t h = 0; h < heads; ++h) {
+      double *o = out + (i * heads + h) * dim;
+      for (int64_t d = 0; d < dim; ++d) o[d] = 0.0;
+      if (n == 0) continue;
+      double m = -INFINITY;
+      for (int64_t c = 0; c < n; ++c) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < dim; ++d)
+          dot += (double)q[(i * heads + h) * dim + d] * (double)kc[(cell[c] * heads + h) * dim + d];
+        s[c] = scale * dot;
+        if (s[c] > m) m = s[c];
+      }
+      double l = 0.0;
+      for (int64_t c = 0; c < n; ++c) {
+        const double w = exp(s[c] - m);
+        l += w;
+        for (int64_t d = 0; d < dim; ++d) o[d] += w * (double)vc[(cell[c] * heads + h) * dim + d];
+      }
+      for (int64_t d = 0; d < dim; ++d) o[d] /= l;
+    }
+  }
+  free(s);
+  free(cell);
   return ORACLE_OK;
 }

@@ -9,6 +9,7 @@ the oracle's C source and shows that every one fails some pin.
 """
 from __future__ import annotations
 
+import math
 import os
 import random
 import re
@@ -190,9 +191,126 @@ def pin_active_rows_only(orc):
     return None
 
 
+# ------------------------------------------ decode attention pins ----
+# (page "#3102 perf(hip): enable wave32 QSA decode attention and MMVQ row reuse
+# on gfx12", Summary item 1: attention of each query over the cells of its
+# selected blocks; the formula is scaled dot-product attention per head)
+
+POISON = 1e30  # finite, so a mutant that reads masked cells changes the result without NaN
+
+
+def attn_case(rng, nq, heads, dim, n_cells, extra=8):
+    q = rng.standard_normal((nq, heads, dim)).astype(np.float32)
+    kc = rng.standard_normal((n_cells + extra, heads, dim)).astype(np.float32)
+    vc = rng.standard_normal((n_cells + extra, heads, dim)).astype(np.float32)
+    kc[n_cells:] = POISON
+    vc[n_cells:] = POISON
+    return q, kc, vc
+
+
+def numpy_attn(q, kc, vc, ids, n_cells, scale):
+    """Vectorised FP64 attention written independently of the oracle's loops."""
+    nq, heads, dim = q.shape
+    out = np.zeros((nq, heads, dim))
+    for i in range(nq):
+        cells = np.array([4 * b + e for b in ids[i] if b >= 0 for e in range(4)
+                          if 4 * b + e < n_cells], dtype=np.int64)
+        if cells.size == 0:
+            continue
+        kk = kc[cells].astype(np.float64)            # [n][heads][dim]
+        vv = vc[cells].astype(np.float64)
+        s = scale * np.einsum("hd,nhd->hn", q[i].astype(np.float64), kk)
+        w = np.exp(s - s.max(axis=1, keepdims=True))
+        out[i] = np.einsum("hn,nhd->hd", w, vv) / w.sum(axis=1)[:, None]
+    return out
+
+
+def pin_attn_single_cell(orc):
+    """One attended cell: its value row, exactly."""
+    rng = np.random.default_rng(21)
+    q, kc, vc = attn_case(rng, 1, 2, 8, n_cells=9)
+    out = orc.sparse_decode_attn_f64(q, kc, vc, np.array([[2, -1]], np.int32), 9, 0.3)
+    if not np.array_equal(out[0], vc[8].astype(np.float64)):
+        return "single attended cell does not return its value row"
+    return None
+
+
+def pin_attn_uniform_weights(orc):
+    """q = 0: every weight is 1, the output is the exact mean of the attended rows."""
+    rng = np.random.default_rng(22)
+    q, kc, vc = attn_case(rng, 1, 2, 4, n_cells=10)
+    q[:] = 0
+    ids = np.array([[0, 2]], np.int32)  # cells 0-3 and 8, 9 (10, 11 masked)
+    out = orc.sparse_decode_attn_f64(q, kc, vc, ids, 10, 1.0)
+    cells = [0, 1, 2, 3, 8, 9]
+    for h in range(2):
+        for d in range(4):
+            exact = sum(Fraction(float(vc[c, h, d])) for c in cells) / len(cells)
+            if abs(Fraction(out[0, h, d]) - exact) > Fraction(1, 2**50) * max(1, abs(exact)):
+                return f"uniform weights: head {h} dim {d} is not the mean"
+    return None
+
+
+def pin_attn_numpy(orc):
+    """Random tiny cases (padding, a repeated block, a partial last block) vs numpy."""
+    rng = np.random.default_rng(23)
+    for nq, heads, dim, n_cells, ids in [
+            (2, 3, 8, 22, [[5, -1, 0, 3], [1, 1, -1, 4]]),
+            (1, 1, 4, 7, [[1, 0, -1, -1]]),
+            (3, 2, 16, 40, [[9, 2, 7, 0], [-1, -1, -1, -1], [3, 8, 6, 1]])]:
+        q, kc, vc = attn_case(rng, nq, heads, dim, n_cells)
+        ids = np.array(ids, np.int32)
+        got = orc.sparse_decode_attn_f64(q, kc, vc, ids, n_cells, 0.25)
+        want = numpy_attn(q, kc, vc, ids, n_cells, 0.25)
+        if not np.allclose(got, want, rtol=1e-12, atol=1e-12):
+            return f"differs from numpy at nq={nq} heads={heads} dim={dim}"
+    return None
+
+
+def pin_attn_two_cells_closed_form(orc):
+    """Two cells with scores 1000 and 998: weights 1/(1+e^-2) and e^-2/(1+e^-2)."""
+    q = np.zeros((1, 1, 4), np.float32)
+    q[0, 0, 0] = 1.0
+    kc = np.zeros((8, 1, 4), np.float32)
+    kc[0, 0, 0], kc[1, 0, 0] = 1000.0, 998.0
+    vc = np.zeros((8, 1, 4), np.float32)
+    vc[0, 0] = [1, 2, 3, 4]
+    vc[1, 0] = [-4, 0, 0.5, 8]
+    kc[2:] = POISON
+    vc[2:] = POISON
+    out = orc.sparse_decode_attn_f64(q, kc, vc, np.array([[0]], np.int32), 2, 1.0)
+    e = math.exp(-2.0)
+    want = (vc[0, 0].astype(np.float64) + e * vc[1, 0].astype(np.float64)) / (1 + e)
+    if not np.allclose(out[0, 0], want, rtol=1e-15, atol=1e-15):
+        return "two-cell closed form"
+    return None
+
+
+def pin_attn_invariants(orc):
+    """List order does not matter; padding and power-of-two value scaling are exact."""
+    rng = np.random.default_rng(24)
+    q, kc, vc = attn_case(rng, 2, 2, 8, n_cells=30)
+    ids = np.array([[6, 0, 3, 5], [2, 7, 1, 4]], np.int32)
+    base = orc.sparse_decode_attn_f64(q, kc, vc, ids, 30, 0.5)
+    if not np.allclose(orc.sparse_decode_attn_f64(q, kc, vc, ids[:, ::-1].copy(), 30, 0.5), base,
+                       rtol=1e-13, atol=1e-13):
+        return "block order changes the result"
+    padded = np.array([[6, -1, 0, 3, -1, 5], [-1, 2, 7, 1, 4, -1]], np.int32)
+    if not np.array_equal(orc.sparse_decode_attn_f64(q, kc, vc, padded, 30, 0.5), base):
+        return "padding changes the result"
+    if not np.array_equal(orc.sparse_decode_attn_f64(q, kc, vc * 2, ids, 30, 0.5), base * 2):
+        return "value scaling is not exact"
+    empty = orc.sparse_decode_attn_f64(q, kc, vc, np.full((2, 3), -1, np.int32), 30, 0.5)
+    if not np.all(empty == 0):
+        return "no attended cell must give zeros"
+    return None
+
+
 PINS = [pin_hand_example, pin_integer_exact, pin_float64_matmul, pin_exact_rationals,
         pin_topk_brute_force, pin_topk_lexsort, pin_topk_special_rows,
-        pin_topk_invariants, pin_active_rows_only]
+        pin_topk_invariants, pin_active_rows_only, pin_attn_single_cell,
+        pin_attn_uniform_weights, pin_attn_numpy, pin_attn_two_cells_closed_form,
+        pin_attn_invariants]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -288,6 +406,13 @@ MUTANTS = {
     "pad with zero": (r": -1;", ": 0;"),
     "signed-zero unequal": (r"c\[b\]\.score = \(double\)s;", "c[b].score = signbit(s) ? -1e-300 : (double)s;"),
     "score via float accumulation": (r"double s = 0\.0;", "float s = 0.0f;"),
+    "attention without the scale": (r"s\[c\] = scale \* dot;", "s[c] = dot;"),
+    "attention reads masked cells": (r"if \(4 \* b \+ e < n_cells\)", "if (4 * b + e <= n_cells)"),
+    "attention divides by the count": (r"o\[d\] /= l;", "o[d] /= (double)n;"),
+    "attention values from the keys": (r"\+= w \* \(double\)vc\[", "+= w * (double)kc["),
+    "attention three cells per block": (r"e < 4; \+\+e", "e < 3; ++e"),
+    "attention without the max shift": (r"exp\(s\[c\] - m\)", "exp(s[c])"),
+    "attention keeps stale output": (r"o\[d\] = 0\.0;", "(void)o;"),
 }
 
 
