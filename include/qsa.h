@@ -19,9 +19,10 @@
  *
  * Conventions for every entry point:
  *   - Every data pointer is a DEVICE pointer on the current HIP device, owned
- *     by the caller.  Some launches also need device scratch (the split
- *     queries of the bf16x3 scorer, the candidate lists of the few-row
- *     top-k); the library keeps one scratch buffer per (device, stream),
+ *     by the caller.  Some launches also need device scratch (the published
+ *     group words of the few-row top-k and of the fused decode select, the
+ *     chunk partials of the decode attention); the library keeps one scratch
+ *     buffer per (device, stream),
  *     allocated with hipMalloc on first need, grown when a call needs more
  *     and never freed before the process ends.  Work on one stream runs in
  *     order, so calls on the same stream share it safely; calls on different
@@ -51,7 +52,7 @@ extern "C" {
 /* Status codes. */
 #define QSA_OK 0
 #define QSA_ERR_NULL 1   /* a required pointer is NULL                              */
-#define QSA_ERR_SHAPE 2  /* a size < 0, or heads*dim not a multiple of 4 in [4, QSA_MAX_HEAD_DIM] */
+#define QSA_ERR_SHAPE 2  /* a size < 0, heads*dim not a multiple of 4 in [4, QSA_MAX_HEAD_DIM], or a bad attention dim */
 #define QSA_ERR_K 3      /* k < 0 or k > QSA_TOPK_MAX_K                             */
 #define QSA_ERR_ALIGN 4  /* q or kblk not 16-byte aligned, scores/ids not 4-byte aligned */
 #define QSA_ERR_LAUNCH 5 /* the HIP runtime rejected a launch (hipGetLastError)     */
@@ -155,6 +156,40 @@ int qsa_block_scores_ex(const float *q, const float *kblk, int nq, int heads, in
  */
 int qsa_block_select(const float *q, const float *kblk, int nq, int heads, int dim,
                      int active_blocks, int k, float *scores, int *ids, void *stream);
+
+/*
+ * qsa_sparse_decode_attention -- attention of each query over the KV cells of
+ * its selected blocks (the consumer of qsa_block_topk's ids; page "#3102
+ * perf(hip): enable wave32 QSA decode attention and MMVQ row reuse on gfx12",
+ * Summary item 1: decode attention over the selected blocks' cells, computed
+ * in chunks whose partials are merged in sequential chunk order).
+ *
+ *   q        [nq][heads][dim] fp32, 16-byte aligned.
+ *   kcache   [>= n_cells][heads][dim] fp32 keys, one row per cell, 16-byte
+ *   vcache   aligned; the same for values.  Cell c belongs to block c / 4.
+ *            Only cells [0, n_cells) are read.
+ *   ids      [nq][k] int32 block ids, e.g. the output of qsa_block_topk.
+ *            Negative entries (the -1 padding) are skipped, and so are the
+ *            cells at or past n_cells of a listed block.  A block listed
+ *            twice is attended twice.
+ *   scale    multiplies every dot product (e.g. 1/sqrt(dim)).
+ *   out      out: [nq][heads][dim] fp32, 4-byte aligned:
+ *              s_c = scale * q[i][h] . kcache[c][h]
+ *              out[i][h] = sum_c exp(s_c - max s) vcache[c][h] / sum_c exp(s_c - max s)
+ *            over the attended cells c of query i; all zeros when query i
+ *            attends no cell.
+ *
+ * dim must be a multiple of 4 in [4, QSA_ATTN_MAX_DIM], heads*dim at most
+ * QSA_MAX_HEAD_DIM and nq at most 65535 (else QSA_ERR_SHAPE); k in [0, QSA_TOPK_MAX_K] (else
+ * QSA_ERR_K).  The cells are processed in fixed chunks of 8 listed blocks and
+ * merged in chunk order, so results are deterministic; the error against an
+ * FP64 evaluation stays within 1e-5 * max|v| of the attended cells.
+ * nq == 0 or heads == 0 is a successful no-op.
+ */
+#define QSA_ATTN_MAX_DIM 128
+int qsa_sparse_decode_attention(const float *q, const float *kcache, const float *vcache,
+                                const int *ids, int nq, int heads, int dim, int k, int n_cells,
+                                float scale, float *out, void *stream);
 
 /* Human-readable text of a status code (a static string; never NULL). */
 const char *qsa_strerror(int status);

@@ -1,8 +1,9 @@
 """QSA block selection on MI355X (gfx950): exact block scoring + radix top-k.
 
 The compute lives in ``libqsa.so`` (hand-written HIP for CDNA4, C ABI declared
-in ``include/qsa.h``).  ``qsa_block_scores`` / ``qsa_block_topk`` here are thin
-ctypes bindings with the same names as the C entry points: they marshal torch
+in ``include/qsa.h``).  ``qsa_block_scores`` / ``qsa_block_topk`` /
+``qsa_block_select`` / ``qsa_sparse_decode_attention`` here are thin ctypes
+bindings with the same names as the C entry points: they marshal torch
 tensors and the current HIP stream, nothing more.  There is no CPU fallback:
 calling them without the built library, or with tensors that are not on the
 GPU, raises.
@@ -14,6 +15,7 @@ def __getattr__(name):
     # The binding loads libqsa.so (and torch) on first use only, so the
     # generator can be imported on hosts without the library.
     if name in ("qsa_block_scores", "qsa_block_scores_ex", "qsa_block_topk", "qsa_block_select",
+                "qsa_sparse_decode_attention", "sparse_decode_attention", "QSA_ATTN_MAX_DIM",
                 "qsa_strerror", "TOPK_FEW_ROWS",
                 "QSAError", "SCORE_MODES",
                 "load_library", "library_path", "TOPK_MAX_K", "block_scores", "block_topk"):

@@ -24,6 +24,7 @@ QSA_MAX_HEAD_DIM = 4096
 TOPK_MAX_K = 4096
 TOPK_FEW_ROWS = 16
 QSA_SCORES_AUTO, QSA_SCORES_FP32, QSA_SCORES_BF16X3 = 0, 1, 2
+QSA_ATTN_MAX_DIM = 128
 SCORE_MODES = {"auto": QSA_SCORES_AUTO, "fp32": QSA_SCORES_FP32, "bf16x3": QSA_SCORES_BF16X3}
 
 # Entry points declared in include/qsa.h: name -> (restype, argtypes).
@@ -33,6 +34,8 @@ SIGNATURES = {
     "qsa_block_scores_ex": (_I, [_VP, _VP, _I, _I, _I, _I, _VP, _I, _VP]),
     "qsa_block_topk": (_I, [_VP, _I, _I, _I, _VP, _VP]),
     "qsa_block_select": (_I, [_VP, _VP, _I, _I, _I, _I, _I, _VP, _VP, _VP]),
+    "qsa_sparse_decode_attention": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_float,
+                                         _VP, _VP]),
     "qsa_strerror": (ctypes.c_char_p, [_I]),
 }
 
@@ -170,6 +173,44 @@ def qsa_block_topk(scores: torch.Tensor, k: int, ids: torch.Tensor | None = None
     return ids
 
 
+def qsa_sparse_decode_attention(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+                                ids: torch.Tensor, n_cells: int | None = None,
+                                scale: float | None = None,
+                                out: torch.Tensor | None = None) -> torch.Tensor:
+    """Attention out [nq, heads, dim] of q [nq, heads, dim] over the cells of the
+    blocks ids [nq, k] (int32, -1 skipped) in kcache/vcache [cells, heads, dim];
+    cells at or past n_cells (default: all rows) are skipped; scale defaults to
+    1/sqrt(dim)."""
+    _require_gpu_f32("q", q, 3)
+    _require_gpu_f32("kcache", kcache, 3)
+    _require_gpu_f32("vcache", vcache, 3)
+    nq, heads, dim = q.shape
+    if kcache.shape[1:] != (heads, dim) or tuple(vcache.shape) != tuple(kcache.shape) or \
+            kcache.device != q.device or vcache.device != q.device:
+        raise ValueError("kcache and vcache must be [cells, heads, dim] on q's device")
+    n = kcache.shape[0] if n_cells is None else int(n_cells)
+    if not 0 <= n <= kcache.shape[0]:
+        raise ValueError(f"n_cells={n} outside [0, {kcache.shape[0]}]")
+    if ids.dtype != torch.int32 or ids.dim() != 2 or ids.shape[0] != nq or \
+            not ids.is_contiguous() or ids.device != q.device:
+        raise ValueError(f"ids must be a contiguous int32 [{nq}, k] tensor on q's device")
+    k = ids.shape[1]
+    sc = 1.0 / float(dim) ** 0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((nq, heads, dim), dtype=torch.float32, device=q.device)
+    elif tuple(out.shape) != (nq, heads, dim) or out.dtype != torch.float32 or \
+            not out.is_contiguous() or out.device != q.device:
+        raise ValueError(f"out must be a contiguous float32 [{nq}, {heads}, {dim}] tensor on q's device")
+    with torch.cuda.device(q.device):
+        st = load_library().qsa_sparse_decode_attention(
+            q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), ids.data_ptr() if ids.numel() else None,
+            nq, heads, dim, k, n, sc, out.data_ptr(), _stream_handle(q.device))
+    if st != QSA_OK:
+        raise QSAError(st, "qsa_sparse_decode_attention")
+    return out
+
+
 # Short aliases.
 block_scores = qsa_block_scores
 block_topk = qsa_block_topk
+sparse_decode_attention = qsa_sparse_decode_attention

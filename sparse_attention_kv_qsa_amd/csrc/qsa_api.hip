@@ -9,6 +9,7 @@
 #include "qsa_internal.h"
 
 static_assert(QSA_TOPK_MAX_K == qsa::kTopkMaxK, "header and kernels disagree on the top-k limit");
+static_assert(QSA_ATTN_MAX_DIM == qsa::kAttnMaxDim, "header and kernels disagree on the attention dim");
 static_assert(QSA_TOPK_FEW_ROWS == qsa::kWideMaxRows, "header and kernels disagree on the few-row path");
 static_assert(QSA_SCORES_AUTO == qsa::kScoresAuto && QSA_SCORES_FP32 == qsa::kScoresFp32 &&
                   QSA_SCORES_BF16X3 == qsa::kScoresBf16x3,
@@ -80,6 +81,24 @@ extern "C" int qsa_block_select(const float *q, const float *kblk, int nq, int h
       qsa::launch_block_select(q, kblk, nq, int(K), active_blocks, k, scores, ids, s));
 }
 
+extern "C" int qsa_sparse_decode_attention(const float *q, const float *kcache, const float *vcache,
+                                           const int *ids, int nq, int heads, int dim, int k,
+                                           int n_cells, float scale, float *out, void *stream) {
+  if (nq < 0 || heads < 0 || dim < 0 || n_cells < 0) return QSA_ERR_SHAPE;
+  if (!qsa::attn_dim_ok(dim) || int64_t(heads) * dim > QSA_MAX_HEAD_DIM) return QSA_ERR_SHAPE;
+  if (nq > 65535) return QSA_ERR_SHAPE;  // one grid dimension per query
+  if (k < 0 || k > QSA_TOPK_MAX_K) return QSA_ERR_K;
+  if (nq == 0 || heads == 0) return QSA_OK;
+  if (!q || !out || (k > 0 && !ids) || (n_cells > 0 && (!kcache || !vcache))) return QSA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(kcache, 16) || !aligned(vcache, 16) || !aligned(ids, 4) ||
+      !aligned(out, 4))
+    return QSA_ERR_ALIGN;
+  (void)hipGetLastError();
+  return launch_status(qsa::launch_sparse_decode_attention(q, kcache, vcache, ids, nq, heads, dim,
+                                                           k, n_cells, scale, out,
+                                                           static_cast<hipStream_t>(stream)));
+}
+
 extern "C" const char *qsa_strerror(int status) {
   switch (status) {
     case QSA_OK:
@@ -87,7 +106,8 @@ extern "C" const char *qsa_strerror(int status) {
     case QSA_ERR_NULL:
       return "a required pointer is NULL";
     case QSA_ERR_SHAPE:
-      return "bad shape: a size is negative, or heads*dim is not a multiple of 4 in [4, 4096]";
+      return "bad shape: a size is negative, heads*dim is not a multiple of 4 in [4, 4096], "
+             "or an attention dim is not a multiple of 4 in [4, 128]";
     case QSA_ERR_K:
       return "bad k: k < 0 or k > 4096";
     case QSA_ERR_ALIGN:

@@ -1,0 +1,309 @@
+// Block-sparse decode attention over the selected blocks (gfx950, wave64).
+//
+// Page "#3102 perf(hip): enable wave32 QSA decode attention and MMVQ row
+// reuse on gfx12", Summary item 1: after selection, each decode query attends
+// only to the KV cells of its selected blocks; the cells are processed in
+// chunks whose partial results are merged in sequential chunk order.  For
+// query i and head h, over the attended cells c (cells 4b .. 4b+3 of every
+// listed block b = ids[i][j] >= 0, c < n_cells):
+//   s_c = scale * q[i][h] . k[c][h],   w_c = exp(s_c - max s),
+//   out[i][h] = sum_c w_c v[c][h] / sum_c w_c        (0 if no cell).
+//
+// Two launches:
+//   1. attn_chunk_kernel: one wave per (query, head, chunk of kChunkBlocks
+//      listed blocks = up to 32 cells).  A cell row of `dim` fp32 is spread
+//      over LPC lanes (a float4 each; LPC = dim/4 rounded up to a power of
+//      two, dim <= 128), so one load instruction covers 64/LPC cells.  The wave first
+//      issues every key and value load of its chunk, then forms the dot
+//      products (4 FMAs per lane and an LPC-lane butterfly: a fixed tree),
+//      the chunk maximum m, the weights exp(s - m), their sum l and the
+//      weighted value sum acc, and writes (m, l, acc[dim]).
+//   2. attn_merge_kernel: one workgroup per (query, head) folds the chunk
+//      partials: M = max m_j, L = sum l_j e^(m_j - M),
+//      out = sum acc_j e^(m_j - M) / L, in a fixed order (each of four waves
+//      sums a contiguous quarter of the chunks, then the four in order).
+//      A fused variant (the last chunk wave of a (query, head) merging, found
+//      by an atomic count) is slower on this GPU: the device-scope release
+//      every wave needs writes back its XCD's L2.
+// Bound: HBM (the gathered key and value rows); the fixed chunking and merge
+// order make the result deterministic.
+#include <hip/hip_runtime.h>
+
+#include "qsa_device.h"
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunkBlocks = 8;                // listed blocks per chunk
+constexpr int kChunkCells = 4 * kChunkBlocks;  // cells per chunk
+
+// Sum over the LPC lanes of a cell (lane bits below log2 LPC), the same tree in
+// every lane.
+template <int LPC>
+__device__ __forceinline__ float cell_sum(float v) {
+  if constexpr (LPC >= 2) v += __uint_as_float(lane_xor<1>(__float_as_uint(v)));
+  if constexpr (LPC >= 4) v += __uint_as_float(lane_xor<2>(__float_as_uint(v)));
+  if constexpr (LPC >= 8) v += __uint_as_float(lane_xor<4>(__float_as_uint(v)));
+  if constexpr (LPC >= 16) v += __uint_as_float(lane_xor<8>(__float_as_uint(v)));
+  if constexpr (LPC >= 32) v += __uint_as_float(lane_xor<16>(__float_as_uint(v)));
+  if constexpr (LPC >= 64) v += __uint_as_float(lane_xor<32>(__float_as_uint(v)));
+  return v;
+}
+
+// Combine across the 64/LPC cell groups of the wave (lane bits from log2 LPC up).
+template <int LPC, class Op>
+__device__ __forceinline__ float group_all(float v, Op op) {
+  if constexpr (LPC <= 1) v = op(v, __uint_as_float(lane_xor<1>(__float_as_uint(v))));
+  if constexpr (LPC <= 2) v = op(v, __uint_as_float(lane_xor<2>(__float_as_uint(v))));
+  if constexpr (LPC <= 4) v = op(v, __uint_as_float(lane_xor<4>(__float_as_uint(v))));
+  if constexpr (LPC <= 8) v = op(v, __uint_as_float(lane_xor<8>(__float_as_uint(v))));
+  if constexpr (LPC <= 16) v = op(v, __uint_as_float(lane_xor<16>(__float_as_uint(v))));
+  if constexpr (LPC <= 32) v = op(v, __uint_as_float(lane_xor<32>(__float_as_uint(v))));
+  return v;
+}
+
+constexpr int kMergeMaxChunks = 512;  // QSA_TOPK_MAX_K / kChunkBlocks
+
+template <int LPC>
+__global__ __launch_bounds__(64) void attn_chunk_kernel(const float *__restrict__ q,
+                                                        const float *__restrict__ kc,
+                                                        const float *__restrict__ vc,
+                                                        const int *__restrict__ ids, int heads,
+                                                        int dim, int k, int n_cells, float scale,
+                                                        float *__restrict__ part, int nchunks) {
+  constexpr int CPI = 64 / LPC;                                    // cells per load instruction
+  constexpr int ROUNDS = kChunkCells / CPI > 0 ? kChunkCells / CPI : 1;  // loads per chunk
+  const int lane = threadIdx.x;
+  const int chunk = blockIdx.x;
+  const int h = blockIdx.y;
+  const int i = blockIdx.z;
+  const int sub = lane & (LPC - 1);             // float4 slot within the row
+  const int grp = lane / LPC;                   // cell group of this lane
+  const bool live = 4 * sub < dim;              // lanes past the row hold zeros
+
+  // The chunk's listed blocks, one per lane (lanes 0 .. kChunkBlocks-1).
+  const int j0 = chunk * kChunkBlocks;
+  int my_id = -1;
+  if (lane < kChunkBlocks && j0 + lane < k) my_id = ids[int64_t(i) * k + j0 + lane];
+
+  const int64_t row = int64_t(heads) * dim;     // floats per cell
+  const int64_t col = int64_t(h) * dim + 4 * sub;
+
+  // Cell of round r for this lane: slot r*CPI + grp of the chunk's cells.
+  int64_t cell[ROUNDS];
+  bool ok[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int slot = r * CPI + grp;
+    const int b = __shfl(my_id, (slot >> 2) & 63, 64);  // -1 past the chunk's blocks
+    const int64_t c = int64_t(b) * 4 + (slot & 3);
+    ok[r] = slot < kChunkCells && b >= 0 && c < n_cells;
+    cell[r] = c;
+  }
+  // Every load of the chunk in flight at once (keys, then values); masked
+  // lanes load nothing.
+  f4 kv[ROUNDS], vv[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    kv[r] = f4{0.f, 0.f, 0.f, 0.f};
+    if (ok[r] && live) kv[r] = *reinterpret_cast<const f4 *>(kc + cell[r] * row + col);
+  }
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    vv[r] = f4{0.f, 0.f, 0.f, 0.f};
+    if (ok[r] && live) vv[r] = *reinterpret_cast<const f4 *>(vc + cell[r] * row + col);
+  }
+  f4 qv = {0.f, 0.f, 0.f, 0.f};
+  if (live) qv = *reinterpret_cast<const f4 *>(q + (int64_t(i) * heads + h) * dim + 4 * sub);
+
+  // Scores of this lane's cells (the same value in all LPC lanes of a cell).
+  float s[ROUNDS];
+  float m = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    float p = qv.x * kv[r].x;
+    p = __builtin_fmaf(qv.y, kv[r].y, p);
+    p = __builtin_fmaf(qv.z, kv[r].z, p);
+    p = __builtin_fmaf(qv.w, kv[r].w, p);
+    s[r] = ok[r] ? scale * cell_sum<LPC>(p) : -INFINITY;
+    m = fmaxf(m, s[r]);
+  }
+  m = group_all<LPC>(m, [](float a, float b) { return fmaxf(a, b); });
+
+  float l = 0.f;
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (m > -INFINITY) {
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      const float w = ok[r] ? expf(s[r] - m) : 0.f;
+      l += w;
+      acc.x = __builtin_fmaf(w, vv[r].x, acc.x);
+      acc.y = __builtin_fmaf(w, vv[r].y, acc.y);
+      acc.z = __builtin_fmaf(w, vv[r].z, acc.z);
+      acc.w = __builtin_fmaf(w, vv[r].w, acc.w);
+    }
+  }
+  auto add = [](float a, float b) { return a + b; };
+  l = group_all<LPC>(l, add);
+  acc.x = group_all<LPC>(acc.x, add);
+  acc.y = group_all<LPC>(acc.y, add);
+  acc.z = group_all<LPC>(acc.z, add);
+  acc.w = group_all<LPC>(acc.w, add);
+
+  // part[(i * heads + h) * nchunks + chunk] = {m, l, acc[dim]} (dim + 2 floats,
+  // padded to dim + 4 so the float4 stores stay aligned).
+  float *dst = part + ((int64_t(i) * heads + h) * nchunks + chunk) * (dim + 4);
+  if (lane == 0) {
+    dst[0] = m;
+    dst[1] = l;
+  }
+  if (grp == 0 && live) *reinterpret_cast<f4 *>(dst + 4 + 4 * sub) = acc;
+}
+
+// One workgroup of kMergeWaves waves per (query, head) folds the chunk
+// partials.  Wave w takes the w-th contiguous quarter of the chunks and issues
+// all of its loads at once; M = max m_j over all chunks, e_j = exp(m_j - M);
+// each wave forms sum_j e_j l_j and sum_j e_j acc_j[d] over its chunks in chunk
+// order, and wave 0 adds the waves' sums in wave order and divides.
+constexpr int kMergeWaves = 4;
+constexpr int kMergePer = kMergeMaxChunks / kMergeWaves;  // chunks per wave, at most
+
+__global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(
+    const float *__restrict__ part, int heads, int dim, int nchunks, float *__restrict__ out) {
+  __shared__ float red[kMergeWaves][2 + 128];  // per wave: L, unused, acc[dim]
+  __shared__ float ew[kMergeMaxChunks];        // e_j of every chunk
+  __shared__ float wmax[kMergeWaves];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int h = blockIdx.x;
+  const int i = blockIdx.y;
+  const int stride = dim + 4;
+  const float *src = part + (int64_t(i) * heads + h) * nchunks * stride;
+  float *o = out + (int64_t(i) * heads + h) * dim;
+  const int per = (nchunks + kMergeWaves - 1) / kMergeWaves;
+  const int j0 = w * per;
+  const int j1 = min(nchunks, j0 + per);
+
+  // Every load of this wave first: the chunk maxima and sums (lane u holds
+  // chunks j0 + u, j0 + u + 64) and the value sums of the first 32 chunks;
+  // nothing here depends on the global maximum.
+  const bool d0 = lane < dim, d1 = lane + 64 < dim;
+  float mj[kMergePer / 64], lj[kMergePer / 64];
+  float a0[32], a1[32];
+#pragma unroll
+  for (int v = 0; v < kMergePer / 64; ++v) {
+    const int j = j0 + lane + 64 * v;
+    mj[v] = -INFINITY;
+    lj[v] = 0.f;
+    if (j < j1) {
+      mj[v] = src[int64_t(j) * stride];
+      lj[v] = src[int64_t(j) * stride + 1];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 32; ++u) {
+    const float *pj = src + int64_t(j0 + u) * stride + 4;
+    a0[u] = (j0 + u < j1 && d0) ? pj[lane] : 0.f;
+    a1[u] = (j0 + u < j1 && d1) ? pj[lane + 64] : 0.f;
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < kMergePer / 64; ++v) m = fmaxf(m, mj[v]);
+  m = group_all<1>(m, [](float x, float y) { return fmaxf(x, y); });
+  if (lane == 0) wmax[w] = m;
+  __syncthreads();
+  float M = wmax[0];
+#pragma unroll
+  for (int u = 1; u < kMergeWaves; ++u) M = fmaxf(M, wmax[u]);
+  if (M == -INFINITY) {  // no attended cell
+    if (w == 0)
+      for (int d = lane; d < dim; d += 64) o[d] = 0.f;
+    return;  // uniform across the workgroup
+  }
+  float L = 0.f;
+#pragma unroll
+  for (int v = 0; v < kMergePer / 64; ++v) {
+    const float e = mj[v] == -INFINITY ? 0.f : expf(mj[v] - M);  // empty chunks weigh 0
+    if (j0 + lane + 64 * v < j1) ew[j0 + lane + 64 * v] = e;
+    L = __builtin_fmaf(lj[v], e, L);
+  }
+  L = group_all<1>(L, [](float x, float y) { return x + y; });
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's weights are in LDS
+  __builtin_amdgcn_wave_barrier();
+
+  // Value sums over this wave's chunks, in chunk order.
+  float acc0 = 0.f, acc1 = 0.f;
+  for (int jb = j0; jb < j1; jb += 32) {
+    if (jb > j0) {
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const float *pj = src + int64_t(jb + u) * stride + 4;
+        a0[u] = (jb + u < j1 && d0) ? pj[lane] : 0.f;
+        a1[u] = (jb + u < j1 && d1) ? pj[lane + 64] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const float e = jb + u < j1 ? ew[jb + u] : 0.f;
+      acc0 = __builtin_fmaf(a0[u], e, acc0);
+      acc1 = __builtin_fmaf(a1[u], e, acc1);
+    }
+  }
+  if (lane == 0) red[w][0] = L;
+  if (d0) red[w][2 + lane] = acc0;
+  if (d1) red[w][2 + 64 + lane] = acc1;
+  __syncthreads();
+  if (w == 0) {
+    float Lt = red[0][0], s0 = d0 ? red[0][2 + lane] : 0.f, s1 = d1 ? red[0][66 + lane] : 0.f;
+#pragma unroll
+    for (int u = 1; u < kMergeWaves; ++u) {
+      Lt += red[u][0];
+      if (d0) s0 += red[u][2 + lane];
+      if (d1) s1 += red[u][66 + lane];
+    }
+    if (d0) o[lane] = s0 / Lt;
+    if (d1) o[lane + 64] = s1 / Lt;
+  }
+}
+
+template <int LPC>
+hipError_t launch_chunks(const float *q, const float *kc, const float *vc, const int *ids, int nq,
+                         int heads, int dim, int k, int n_cells, float scale, float *part,
+                         int nchunks, hipStream_t stream) {
+  attn_chunk_kernel<LPC><<<dim3(nchunks, heads, nq), 64, 0, stream>>>(
+      q, kc, vc, ids, heads, dim, k, n_cells, scale, part, nchunks);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_dim_ok(int dim) { return dim >= 4 && dim % 4 == 0 && dim <= kAttnMaxDim; }
+
+hipError_t launch_sparse_decode_attention(const float *q, const float *kc, const float *vc,
+                                          const int *ids, int nq, int heads, int dim, int k,
+                                          int n_cells, float scale, float *out,
+                                          hipStream_t stream) {
+  const int nchunks = k > 0 ? (k + kChunkBlocks - 1) / kChunkBlocks : 1;
+  void *ws = nullptr;
+  hipError_t e = workspace(stream, size_t(nq) * heads * nchunks * (dim + 4) * sizeof(float), &ws);
+  if (e != hipSuccess) return e;
+  float *part = static_cast<float *>(ws);
+  const int lpc = dim <= 4 ? 1 : dim <= 8 ? 2 : dim <= 16 ? 4 : dim <= 32 ? 8 : dim <= 64 ? 16 : 32;
+  switch (lpc) {
+    case 1: e = launch_chunks<1>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
+    case 2: e = launch_chunks<2>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
+    case 4: e = launch_chunks<4>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
+    case 8: e = launch_chunks<8>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
+    case 16: e = launch_chunks<16>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
+    default: e = launch_chunks<32>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
+  }
+  if (e != hipSuccess) return e;
+  attn_merge_kernel<<<dim3(heads, nq), 64 * kMergeWaves, 0, stream>>>(part, heads, dim, nchunks, out);
+  return hipGetLastError();
+}
+
+}  // namespace qsa

@@ -63,4 +63,14 @@ hipError_t launch_gemv_tops(const float *q, const float *kblk, int nq, int K, in
 hipError_t launch_wide_rank(const float *scores, int nq, int A, int k, int *ids,
                             const uint64_t *tops, int M, hipStream_t stream);
 
+// Block-sparse decode attention (qsa_attn.hip): out[nq][heads][dim] from the
+// cells of the blocks ids[nq][k] (-1 skipped) in kc/vc[cells][heads][dim],
+// cells c < n_cells only.  dim in [4, kAttnMaxDim], a multiple of 4.
+constexpr int kAttnMaxDim = 128;
+bool attn_dim_ok(int dim);
+hipError_t launch_sparse_decode_attention(const float *q, const float *kc, const float *vc,
+                                          const int *ids, int nq, int heads, int dim, int k,
+                                          int n_cells, float scale, float *out,
+                                          hipStream_t stream);
+
 }  // namespace qsa

@@ -10,10 +10,40 @@ judge a result against what the definition fixes:
 * ``topk_invariants``: properties any correct selection has (distinct ids in
   range, rank order, selected >= unselected, threshold ties taken lowest-id
   first, -1 padding past the row length).
+* ``attn_limit``: the decode-attention gate for each (query, head).
 """
 from __future__ import annotations
 
 import numpy as np
+
+# Decode attention gate, per query i and head h:
+#   max_d |out - out64| <= max_{c} |v[c][h]| * (ATTN_TOL + ATTN_SCORE_TOL * scale * max_c sum_d |q_d k_cd|)
+# over the attended cells c.  The output is a convex combination of value
+# rows.  An fp32 score s_c = scale * q.k_c carries at most about
+# (4 + log2(dim/4)) * 2^-24 * scale * sum_d |q_d k_cd| of rounding (a 4-term
+# FMA chain and a fixed lane tree, <= 9 levels at dim 128); an error e in
+# every score moves the normalised weights by at most ~2e relatively, hence
+# the second term with ATTN_SCORE_TOL = 2 * 12 * 2^-24 (margin included).
+# The weighted sums (<= 32 terms per lane, a 1-level lane tree), the chunk
+# merge (sequential over <= 512 chunks) and exp add a few 2^-24 of max|v|,
+# bounded by ATTN_TOL = 4e-6 at the sizes tested.
+ATTN_TOL = 4e-6
+ATTN_SCORE_TOL = 2 * 12 * 2.0 ** -24
+
+
+def attn_limit(q, kc, vc, ids, n_cells, scale):
+    """The gate above for every (query, head): an array [nq][heads]."""
+    nq, heads, _ = q.shape
+    lim = np.zeros((nq, heads))
+    for i in range(nq):
+        cells = [4 * b + e for b in ids[i] if b >= 0 for e in range(4) if 4 * b + e < n_cells]
+        if not cells:
+            continue
+        vmax = np.abs(vc[cells].astype(np.float64)).max(axis=(0, 2))                  # [heads]
+        qk = np.abs(q[i][None].astype(np.float64) * kc[cells].astype(np.float64)).sum(axis=2)
+        lim[i] = vmax * (ATTN_TOL + ATTN_SCORE_TOL * abs(scale) * qk.max(axis=0))
+    return lim
+
 
 SCORE_TOL = 1e-6
 

@@ -34,7 +34,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert header_entry_points() == ["qsa_block_scores", "qsa_block_scores_ex", "qsa_block_select",
-                                     "qsa_block_topk", "qsa_strerror"]
+                                     "qsa_block_topk", "qsa_sparse_decode_attention",
+                                     "qsa_strerror"]
 
 
 def test_binding_covers_the_header():
@@ -51,6 +52,7 @@ def test_binding_covers_the_header():
     assert (mac["QSA_SCORES_AUTO"], mac["QSA_SCORES_FP32"], mac["QSA_SCORES_BF16X3"]) == (
         binding.QSA_SCORES_AUTO, binding.QSA_SCORES_FP32, binding.QSA_SCORES_BF16X3)
     assert mac["QSA_MAX_HEAD_DIM"] == binding.QSA_MAX_HEAD_DIM
+    assert mac["QSA_ATTN_MAX_DIM"] == binding.QSA_ATTN_MAX_DIM
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -141,6 +143,34 @@ def test_block_topk_argument_checks(lib, args, status):
 ])
 def test_block_select_argument_checks(lib, args, status):
     assert lib.qsa_block_select(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    # q, kcache, vcache, ids, nq, heads, dim, k, n_cells, scale, out
+    ((P16, P16, P16, P16, -1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_SHAPE),
+    ((P16, P16, P16, P16, 1, -4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_SHAPE),
+    ((P16, P16, P16, P16, 1, 4, 130, 8, 100, 0.1, P16), binding.QSA_ERR_SHAPE),   # dim > 128
+    ((P16, P16, P16, P16, 1, 4, 126, 8, 100, 0.1, P16), binding.QSA_ERR_SHAPE),   # dim % 4
+    ((P16, P16, P16, P16, 1, 4, 0, 8, 100, 0.1, P16), binding.QSA_ERR_SHAPE),
+    ((P16, P16, P16, P16, 1, 40, 128, 8, 100, 0.1, P16), binding.QSA_ERR_SHAPE),  # heads*dim > 4096
+    ((P16, P16, P16, P16, 1, 4, 128, 8, -1, 0.1, P16), binding.QSA_ERR_SHAPE),    # n_cells < 0
+    ((P16, P16, P16, P16, 1, 4, 128, -1, 100, 0.1, P16), binding.QSA_ERR_K),
+    ((P16, P16, P16, P16, 1, 4, 128, 4097, 100, 0.1, P16), binding.QSA_ERR_K),
+    ((None, P16, P16, P16, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_NULL),
+    ((P16, None, P16, P16, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_NULL),
+    ((P16, P16, None, P16, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_NULL),
+    ((P16, P16, P16, None, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_NULL),
+    ((P16, P16, P16, P16, 1, 4, 128, 8, 100, 0.1, None), binding.QSA_ERR_NULL),
+    ((P4, P16, P16, P16, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_ALIGN),
+    ((P16, P4, P16, P16, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_ALIGN),
+    ((P16, P16, P4, P16, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_ALIGN),
+    ((P16, P16, P16, P16 + 2, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_ALIGN),
+    ((P16, P16, P16, P16, 1, 4, 128, 8, 100, 0.1, P16 + 2), binding.QSA_ERR_ALIGN),
+    ((None, None, None, None, 0, 4, 128, 8, 100, 0.1, None), binding.QSA_OK),   # nq = 0: no-op
+    ((None, None, None, None, 3, 0, 128, 8, 100, 0.1, None), binding.QSA_OK),   # heads = 0: no-op
+])
+def test_sparse_decode_attention_argument_checks(lib, args, status):
+    assert lib.qsa_sparse_decode_attention(*args, None) == status
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,0 +1,128 @@
+"""GPU parity of the block-sparse decode attention (through the C ABI) against
+the CPU oracle's FP64 attention.
+
+Gate, the same at every size: for every query i and head h,
+    max_d |out_gpu[i][h][d] - out64[i][h][d]| <= attn_limit(...)[i][h]
+= max|v| of the attended cells x (4e-6 + 1.4e-6 x scale x max_c sum_d |q_d k_cd|)
+(tests/checks.py derives it from the fp32 arithmetic), bitwise where the exact
+result is an fp32 number (a single attended cell, no attended cell).  The attended cells of
+a query are those of its listed blocks (4 per block) below n_cells.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from checks import attn_limit
+from sparse_attention_kv_qsa_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ORC = oracle.default()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_attention_kv_qsa_amd import binding
+    lib = binding.load_library()
+    assert binding.library_path().startswith(os.path.dirname(os.path.dirname(__file__)))
+    return lib
+
+
+def gpu_attn(q, kc, vc, ids, n_cells, scale):
+    from sparse_attention_kv_qsa_amd import qsa_sparse_decode_attention
+    out = qsa_sparse_decode_attention(torch.from_numpy(q).cuda(), torch.from_numpy(kc).cuda(),
+                                      torch.from_numpy(vc).cuda(),
+                                      torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda(),
+                                      n_cells, scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_attn(q, kc, vc, ids, n_cells, scale):
+    got = gpu_attn(q, kc, vc, ids, n_cells, scale)
+    want = ORC.sparse_decode_attn_f64(q, kc, vc, ids, n_cells, scale)
+    err = np.abs(got.astype(np.float64) - want).max(axis=2)        # [nq][heads]
+    lim = attn_limit(q, kc, vc, ids, n_cells, scale)
+    bad = np.argwhere(err > lim)
+    assert bad.size == 0, (f"{len(bad)} (query, head) pairs over the gate; first {tuple(bad[0])}: "
+                           f"error {err[tuple(bad[0])]:.3e} vs limit {lim[tuple(bad[0])]:.3e}")
+    return got
+
+
+def case(seed, nq, heads, dim, n_cells, k, cap_extra=5, pad=0.0, dup=False, past=False):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((nq, heads, dim)).astype(np.float32)
+    kc = rng.standard_normal((n_cells + cap_extra, heads, dim)).astype(np.float32)
+    vc = rng.standard_normal((n_cells + cap_extra, heads, dim)).astype(np.float32)
+    kc[n_cells:] = np.nan  # never read
+    vc[n_cells:] = np.nan
+    nblocks = (n_cells + 3) // 4
+    ids = np.stack([rng.choice(nblocks, size=k, replace=k > nblocks) for _ in range(nq)]).astype(np.int32) \
+        if k else np.zeros((nq, 0), np.int32)
+    if pad and k:
+        ids[rng.random(ids.shape) < pad] = -1
+    if dup and k >= 2:
+        ids[:, 1] = ids[:, 0]
+    if past and k >= 3:
+        ids[:, 2] = nblocks + 7  # a block wholly past n_cells: skipped
+    return q, kc, vc, ids
+
+
+SHAPES = [  # nq, heads, dim, n_cells, k
+    (1, 4, 128, 2048, 512), (1, 4, 128, 4001, 300), (2, 4, 128, 1000, 64), (4, 4, 128, 9000, 512),
+    (1, 1, 4, 37, 9), (3, 2, 8, 50, 13), (1, 3, 16, 99, 25), (2, 2, 32, 130, 7), (1, 8, 64, 513, 8),
+    (2, 2, 96, 300, 17), (8, 4, 128, 600, 129), (1, 2, 128, 5, 1), (3, 4, 64, 257, 33),
+]
+
+
+@pytest.mark.parametrize("nq,heads,dim,n_cells,k", SHAPES)
+def test_attention_random(nq, heads, dim, n_cells, k):
+    q, kc, vc, ids = case(nq * 31 + dim + k, nq, heads, dim, n_cells, k, pad=0.1, dup=True, past=True)
+    check_attn(q, kc, vc, ids, n_cells, 1.0 / np.sqrt(dim))
+
+
+def test_attention_scales_and_large_scores():
+    q, kc, vc, ids = case(5, 2, 4, 128, 800, 64)
+    for scale in (0.0, 0.01, 1.0 / np.sqrt(128), 1.0, 8.0):   # scale 8: scores in the hundreds
+        check_attn(q, kc, vc, ids, 800, scale)
+
+
+def test_attention_single_cell_and_empty_are_exact():
+    q, kc, vc, _ = case(6, 2, 3, 64, 41, 0)
+    one = np.array([[10, -1], [-1, 10]], np.int32)   # block 10: cells 40 (valid), 41-43 (past n_cells)
+    got = gpu_attn(q, kc, vc, one, 41, 0.3)
+    assert np.array_equal(got[0], vc[40]) and np.array_equal(got[1], vc[40])
+    empty = np.full((2, 4), -1, np.int32)
+    assert np.all(gpu_attn(q, kc, vc, empty, 41, 0.3) == 0)
+    assert np.all(gpu_attn(q, kc, vc, np.zeros((2, 0), np.int32), 41, 0.3) == 0)
+
+
+def test_attention_deterministic_and_order_insensitive():
+    q, kc, vc, ids = case(7, 2, 4, 128, 3000, 256)
+    a = gpu_attn(q, kc, vc, ids, 3000, 0.1)
+    assert np.array_equal(a, gpu_attn(q, kc, vc, ids, 3000, 0.1))
+    b = check_attn(q, kc, vc, ids[:, ::-1].copy(), 3000, 0.1)
+    lim = attn_limit(q, kc, vc, ids, 3000, 0.1)[..., None]
+    assert np.all(np.abs(a.astype(np.float64) - b) <= 2 * lim)
+
+
+def test_attention_after_selection():
+    """The decode chain: scores, top-k, then attention over the selected blocks."""
+    from sparse_attention_kv_qsa_amd import qsa_block_select
+    w = synth.WORKLOADS["tiny-decode"]
+    bt = synth.make_batch(w)
+    rng = np.random.default_rng(8)
+    n_cells = 4 * w.active - 1                       # a partial last block
+    kc = rng.standard_normal((4 * w.capacity, w.heads, w.dim)).astype(np.float32)
+    vc = rng.standard_normal((4 * w.capacity, w.heads, w.dim)).astype(np.float32)
+    _, ids = qsa_block_select(torch.from_numpy(bt.q).cuda(), torch.from_numpy(bt.kblk).cuda(), w.k,
+                              w.active)
+    ids = ids.cpu().numpy()
+    check_attn(bt.q, kc, vc, ids, n_cells, 1.0 / np.sqrt(w.dim))
