@@ -20,6 +20,12 @@ select - WMMA block scorer, prompt-aware top-k dispatch", What items 1-2):
   attention of each query and head over the cells of its listed blocks (page
   "#3102 perf(hip): enable wave32 QSA decode attention and MMVQ row reuse on
   gfx12", Summary item 1).
+* ``sparse_decode_attn_i8_f64(q, kcode, kscale, vcode, vscale, ids, n_cells,
+  scale)``: the same attention over an int8 pool (int8 codes, one binary16
+  scale per cell and head; the page above, microbenchmark table, and "#3224
+  [Engine] perf(hip): tune RDNA4 QSA prompt WMMA path (STRATA_HIP_WMMA stays
+  opt-in)", Summary item 2).
+* ``half_to_f64(bits)``: the IEEE binary16 decoding that pool uses.
 
 Every function here is pinned by tests/test_oracle.py (hand example, exact
 integer inputs, exact rationals, numpy float64 matmul, brute-force rank,
@@ -79,6 +85,11 @@ def _bind(path: str):
     lib.oracle_sparse_decode_attn_f64.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                                   ctypes.c_double, vp]
     lib.oracle_sparse_decode_attn_f64.restype = ctypes.c_int
+    lib.oracle_sparse_decode_attn_i8_f64.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                                     i64, ctypes.c_double, vp]
+    lib.oracle_sparse_decode_attn_i8_f64.restype = ctypes.c_int
+    lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_half_to_double.restype = ctypes.c_double
     return lib
 
 
@@ -157,6 +168,36 @@ class Oracle:
                                                       float(scale), _ptr(out)))
         return out
 
+    def sparse_decode_attn_i8_f64(self, q: np.ndarray, kcode: np.ndarray, kscale: np.ndarray,
+                                  vcode: np.ndarray, vscale: np.ndarray, ids: np.ndarray,
+                                  n_cells: int, scale: float) -> np.ndarray:
+        """FP64 attention over an int8 pool: kcode/vcode [cells][heads][dim] int8,
+        kscale/vscale [cells][heads] binary16 bit patterns (uint16)."""
+        q = np.ascontiguousarray(q, dtype=np.float32)
+        kcode = np.ascontiguousarray(kcode, dtype=np.int8)
+        vcode = np.ascontiguousarray(vcode, dtype=np.int8)
+        kscale = np.ascontiguousarray(kscale, dtype=np.uint16)
+        vscale = np.ascontiguousarray(vscale, dtype=np.uint16)
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        nq, heads, dim = q.shape
+        if ids.ndim != 2 or ids.shape[0] != nq:
+            raise ValueError("ids must be [nq][k]")
+        if kcode.shape[1:] != (heads, dim) or vcode.shape != kcode.shape or \
+                kcode.shape[0] < n_cells or kscale.shape != kcode.shape[:2] or \
+                vscale.shape != kscale.shape:
+            raise ValueError("codes must be [>=n_cells][heads][dim], scales [cells][heads]")
+        out = np.empty((nq, heads, dim), dtype=np.float64)
+        _check(self.lib.oracle_sparse_decode_attn_i8_f64(
+            _ptr(q), _ptr(kcode), _ptr(kscale), _ptr(vcode), _ptr(vscale), _ptr(ids), nq, heads,
+            dim, ids.shape[1], n_cells, float(scale), _ptr(out)))
+        return out
+
+    def half_to_f64(self, bits) -> np.ndarray:
+        """Values of binary16 bit patterns (any integer array), as float64."""
+        b = np.asarray(bits, dtype=np.uint16)
+        f = self.lib.oracle_half_to_double
+        return np.array([f(int(x)) for x in b.ravel()], dtype=np.float64).reshape(b.shape)
+
 
 def default() -> Oracle:
     return Oracle(_load())
@@ -181,3 +222,12 @@ def topk_f64(scores, k):
 
 def sparse_decode_attn_f64(q, kc, vc, ids, n_cells, scale):
     return default().sparse_decode_attn_f64(q, kc, vc, ids, n_cells, scale)
+
+
+def sparse_decode_attn_i8_f64(q, kcode, kscale, vcode, vscale, ids, n_cells, scale):
+    return default().sparse_decode_attn_i8_f64(q, kcode, kscale, vcode, vscale, ids, n_cells,
+                                               scale)
+
+
+def half_to_f64(bits):
+    return default().half_to_f64(bits)

@@ -15,6 +15,9 @@
  *        the selected blocks, computed in chunks whose partial results are
  *        merged in sequential chunk order) and the decode-attention
  *        microbenchmark table (attended widths, one or four queries).
+ *   [P2] "#3224 [Engine] perf(hip): tune RDNA4 QSA prompt WMMA path
+ *        (STRATA_HIP_WMMA stays opt-in)", Summary item 2 (an int8 key/value
+ *        pool carries FP16 scales for its keys and values).
  *   [P1] "#3108 perf(hip): optimize exact QSA block scoring and top-k selection
  *        on gfx12", Summary item 1 (a block score is the sum over the query's
  *        heads of per-head dot products against the block's key summary) and
@@ -36,7 +39,11 @@
  *   - decode attention ([P3]): per query and head, scaled dot-product
  *     attention over the cells of the listed blocks (block b holds cells
  *     4b .. 4b+3; cells at or past n_cells and ids of -1 are skipped), with a
- *     caller-given scale; no attended cell gives a zero output.
+ *     caller-given scale; no attended cell gives a zero output;
+ *   - an int8 key/value pool ([P3] microbenchmark table, "int8" pool; [P2]
+ *     Summary item 2: int8 keys and values with FP16 key and value scales)
+ *     holds one signed 8-bit code per (cell, head, d) and one IEEE binary16
+ *     scale per (cell, head); the value it stands for is code * scale.
  *
  * Pins (what this oracle is checked against, not itself): a hand-worked
  * 3-block example, exact integer inputs vs numpy int64 matmul, exact rationals
@@ -223,6 +230,86 @@ int oracle_sparse_decode_attn_f64(const float *q, const float *kc, const float *
         const double w = exp(s[c] - m);
         l += w;
         for (int64_t d = 0; d < dim; ++d) o[d] += w * (double)vc[(cell[c] * heads + h) * dim + d];
+      }
+      for (int64_t d = 0; d < dim; ++d) o[d] /= l;
+    }
+  }
+  free(s);
+  free(cell);
+  return ORACLE_OK;
+}
+
+/*
+ * IEEE 754 binary16 to double, from the format: one sign bit, five exponent
+ * bits with bias 15 and ten fraction bits; exponent 0 holds zero and the
+ * subnormals (fraction * 2^-24), exponent 31 infinity (fraction 0) and NaN.
+ */
+double oracle_half_to_double(uint16_t h) {
+  const int sign = (h >> 15) & 1;
+  const int e = (h >> 10) & 31;
+  const int f = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24);
+  else if (e == 31)
+    v = f == 0 ? INFINITY : NAN;
+  else
+    v = ldexp((double)(1024 + f), e - 25);
+  return sign ? -v : v;
+}
+
+/*
+ * The same attention over an int8 pool ([P3] microbenchmark table, int8 pool;
+ * [P2] Summary item 2): key element (c, h, d) is kcode[c][h][d] *
+ * half(kscale[c][h]), value element vcode[c][h][d] * half(vscale[c][h]); each
+ * is formed in FP64 and the attention is then the one above.  Layouts:
+ * kcode, vcode [cells][heads][dim] int8; kscale, vscale [cells][heads]
+ * binary16 bit patterns.
+ */
+int oracle_sparse_decode_attn_i8_f64(const float *q, const int8_t *kcode, const uint16_t *kscale,
+                                     const int8_t *vcode, const uint16_t *vscale,
+                                     const int32_t *ids, int64_t nq, int64_t heads, int64_t dim,
+                                     int64_t k, int64_t n_cells, double scale, double *out) {
+  if (nq < 0 || heads < 0 || dim < 0 || k < 0 || n_cells < 0) return ORACLE_ERR_ARG;
+  if (nq == 0 || heads == 0 || dim == 0) return ORACLE_OK;
+  if (!q || !out || (k > 0 && (!ids || !kcode || !kscale || !vcode || !vscale)))
+    return ORACLE_ERR_ARG;
+  double *s = (double *)malloc(sizeof(double) * (size_t)(4 * k > 0 ? 4 * k : 1));
+  int64_t *cell = (int64_t *)malloc(sizeof(int64_t) * (size_t)(4 * k > 0 ? 4 * k : 1));
+  if (!s || !cell) {
+    free(s);
+    free(cell);
+    return ORACLE_ERR_NOMEM;
+  }
+  for (int64_t i = 0; i < nq; ++i) {
+    int64_t n = 0;
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t b = ids[i * k + j];
+      if (b < 0) continue;
+      for (int64_t e = 0; e < 4; ++e)
+        if (4 * b + e < n_cells) cell[n++] = 4 * b + e;
+    }
+    for (int64_t h = 0; h < heads; ++h) {
+      double *o = out + (i * heads + h) * dim;
+      for (int64_t d = 0; d < dim; ++d) o[d] = 0.0;
+      if (n == 0) continue;
+      double m = -INFINITY;
+      for (int64_t c = 0; c < n; ++c) {
+        const int64_t r = cell[c] * heads + h;
+        const double ks = oracle_half_to_double(kscale[r]);
+        double dot = 0.0;
+        for (int64_t d = 0; d < dim; ++d)
+          dot += (double)q[(i * heads + h) * dim + d] * ((double)kcode[r * dim + d] * ks);
+        s[c] = scale * dot;
+        if (s[c] > m) m = s[c];
+      }
+      double l = 0.0;
+      for (int64_t c = 0; c < n; ++c) {
+        const int64_t r = cell[c] * heads + h;
+        const double vs = oracle_half_to_double(vscale[r]);
+        const double w = exp(s[c] - m);
+        l += w;
+        for (int64_t d = 0; d < dim; ++d) o[d] += w * ((double)vcode[r * dim + d] * vs);
       }
       for (int64_t d = 0; d < dim; ++d) o[d] /= l;
     }

@@ -20,7 +20,12 @@ data, seeds or test vectors; everything below is synthetic:
   row of scores has at most 64 + n_needle distinct values and ~1,000-way ties
   at the selection threshold;
 * capacity rows past the active blocks hold quiet NaN (poison) so that a
-  kernel that reads them shows it.
+  kernel that reads them shows it;
+* the key and value cells attended after selection (``make_kv``) are N(0, 1)
+  drawn directly in float32 (a cache of a quarter-million cells is too large
+  to draw in float64 first), with the cells past the active blocks poisoned
+  the same way.  The pages give no link between a block's summary and its
+  cells that the timing would depend on, so the two are drawn independently.
 
 Draw order per workload (fixed): q; block summaries (or the tie vectors, then
 their assignment); needle block ids; needle query ids; needle noise.
@@ -147,6 +152,39 @@ def make_random(nq: int, heads: int, dim: int, active: int, capacity: int | None
     if capacity > active:
         kblk[active:] = np.nan if poison else 0.0
     return q, kblk
+
+
+def make_kv(w: Workload, seed: int | None = None):
+    """Key and value caches [4 * capacity, heads, dim] float32 for workload ``w``
+    (cells of the active blocks N(0, 1), the rest quiet NaN if ``w.poison``,
+    else 0).  Draw order: keys, then values, from PCG64(seed + 1)."""
+    base = w.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(base + 1))
+    n, live = 4 * w.capacity, 4 * w.active
+    out = []
+    for _ in range(2):
+        c = np.empty((n, w.heads, w.dim), dtype=np.float32)
+        c[:live] = rng.standard_normal((live, w.heads, w.dim), dtype=np.float32)
+        c[live:] = np.nan if w.poison else 0.0
+        out.append(c)
+    return out[0], out[1]
+
+
+def make_pool_i8(cells: int, live: int, heads: int, dim: int, seed: int = 0,
+                 poison: bool = True):
+    """An int8 key or value pool: codes [cells, heads, dim] int8 and one
+    binary16 scale per (cell, head) as uint16 bit patterns.  Codes are
+    round(N(0, 40)) clipped to [-127, 127] (the spread of a quantised normal
+    row), scales uniform in [0.01, 0.04] rounded to binary16.  Cells at or past
+    `live` get code 0 and, with `poison`, a quiet-NaN scale (0x7E00)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    codes = np.zeros((cells, heads, dim), dtype=np.int8)
+    x = np.rint(rng.standard_normal((live, heads, dim), dtype=np.float32) * 40.0)
+    codes[:live] = np.clip(x, -127, 127).astype(np.int8)
+    scales = np.empty((cells, heads), dtype=np.uint16)
+    scales[:live] = rng.uniform(0.01, 0.04, (live, heads)).astype(np.float16).view(np.uint16)
+    scales[live:] = 0x7E00 if poison else 0
+    return codes, scales
 
 
 def fingerprint(a: np.ndarray) -> str:

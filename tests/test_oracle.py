@@ -306,11 +306,79 @@ def pin_attn_invariants(orc):
     return None
 
 
+# ---------------------------------------------------- int8 pool ----
+# (an int8 key/value pool: one code per (cell, head, d), one binary16 scale
+# per (cell, head); page "#3224 [Engine] perf(hip): tune RDNA4 QSA prompt WMMA
+# path (STRATA_HIP_WMMA stays opt-in)", Summary item 2, and the int8 rows of
+# the decode-attention table of "#3102 perf(hip): ...")
+
+def pin_half_decoding(orc):
+    """The oracle's binary16 decoding agrees with numpy's float16 on all 65,536
+    bit patterns (sign, zeros, subnormals, infinities and NaN included)."""
+    b = np.arange(65536, dtype=np.uint16)
+    ref = b.view(np.float16).astype(np.float64)
+    got = orc.half_to_f64(b)
+    nan = np.isnan(ref)
+    if not np.array_equal(np.isnan(got), nan):
+        return "half decoding: NaN patterns differ"
+    if not np.array_equal(got[~nan], ref[~nan]) or \
+            not np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan])):
+        return "half decoding differs from numpy float16"
+    return None
+
+
+def i8_case(rng, nq, heads, dim, n_cells, extra=8):
+    q = rng.standard_normal((nq, heads, dim)).astype(np.float32)
+    pools = []
+    for _ in range(2):
+        codes = rng.integers(-127, 128, (n_cells + extra, heads, dim)).astype(np.int8)
+        scales = rng.uniform(0.005, 0.05, (n_cells + extra, heads)).astype(np.float16)
+        scales[n_cells:] = np.float16(60000.0)  # masked cells: a huge but finite scale
+        pools += [codes, scales.view(np.uint16)]
+    return q, pools
+
+
+def dequantize(codes, scale_bits):
+    """code * scale, exact in float32 (an 8-bit code times an 11-bit significand)."""
+    return codes.astype(np.float32) * scale_bits.view(np.float16).astype(np.float32)[..., None]
+
+
+def pin_attn_i8_dequantized(orc):
+    """The int8 pool gives the attention of its dequantised fp32 rows: the same
+    FP64 values as the fp32 attention on them, and numpy's within 1e-12."""
+    rng = np.random.default_rng(31)
+    for nq, heads, dim, n_cells, ids in [
+            (2, 3, 8, 22, [[5, -1, 0, 3], [1, 1, -1, 4]]),
+            (3, 2, 16, 40, [[9, 2, 7, 0], [-1, -1, -1, -1], [3, 8, 6, 1]])]:
+        q, (kq, ks, vq, vs) = i8_case(rng, nq, heads, dim, n_cells)
+        ids = np.array(ids, np.int32)
+        got = orc.sparse_decode_attn_i8_f64(q, kq, ks, vq, vs, ids, n_cells, 0.25)
+        kc, vc = dequantize(kq, ks), dequantize(vq, vs)
+        if not np.array_equal(got, orc.sparse_decode_attn_f64(q, kc, vc, ids, n_cells, 0.25)):
+            return f"int8 pool differs from fp32 attention on its dequantised rows (dim={dim})"
+        if not np.allclose(got, numpy_attn(q, kc, vc, ids, n_cells, 0.25), rtol=1e-12, atol=1e-12):
+            return f"int8 pool differs from numpy on its dequantised rows (dim={dim})"
+    return None
+
+
+def pin_attn_i8_single_cell(orc):
+    """One attended cell: code * scale of its value row, exactly, signs included."""
+    rng = np.random.default_rng(32)
+    q, (kq, ks, vq, vs) = i8_case(rng, 1, 2, 8, n_cells=9)
+    vq[8, 1, :4] = [-128, 127, -1, 0]
+    out = orc.sparse_decode_attn_i8_f64(q, kq, ks, vq, vs, np.array([[2, -1]], np.int32), 9, 0.3)
+    want = vq[8].astype(np.float64) * vs[8].view(np.float16).astype(np.float64)[:, None]
+    if not np.array_equal(out[0], want):
+        return "int8 single cell is not code * scale"
+    return None
+
+
 PINS = [pin_hand_example, pin_integer_exact, pin_float64_matmul, pin_exact_rationals,
         pin_topk_brute_force, pin_topk_lexsort, pin_topk_special_rows,
         pin_topk_invariants, pin_active_rows_only, pin_attn_single_cell,
         pin_attn_uniform_weights, pin_attn_numpy, pin_attn_two_cells_closed_form,
-        pin_attn_invariants]
+        pin_attn_invariants, pin_half_decoding, pin_attn_i8_dequantized,
+        pin_attn_i8_single_cell]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -413,6 +481,17 @@ MUTANTS = {
     "attention three cells per block": (r"e < 4; \+\+e", "e < 3; ++e"),
     "attention without the max shift": (r"exp\(s\[c\] - m\)", "exp(s[c])"),
     "attention keeps stale output": (r"o\[d\] = 0\.0;", "(void)o;"),
+    "int8 key scale from the value scales": (r"oracle_half_to_double\(kscale\[r\]\)",
+                                             "oracle_half_to_double(vscale[r])"),
+    "int8 codes read unsigned": (r"\(double\)kcode\[r \* dim \+ d\]",
+                                 "(double)(uint8_t)kcode[r * dim + d]"),
+    "int8 scale per cell, not per head": (r"kscale\[r\]", "kscale[cell[c]]"),
+    "int8 values without their scale": (r"\(\(double\)vcode\[r \* dim \+ d\] \* vs\)",
+                                        "((double)vcode[r * dim + d])"),
+    "half exponent bias off by one": (r"e - 25", "e - 24"),
+    "half subnormals flushed": (r"v = ldexp\(\(double\)f, -24\);", "v = 0.0;"),
+    "half sign dropped": (r"return sign \? -v : v;", "return v;"),
+    "half implicit bit dropped": (r"1024 \+ f", "f"),
 }
 
 

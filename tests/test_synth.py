@@ -62,3 +62,24 @@ def test_full_workload_shapes():
     bt = synth.make_batch(synth.WORKLOADS["prompt-32k"])
     assert bt.q.shape == (256, 4, 128) and bt.kblk.shape == (8193, 4, 128)
     assert bt.q.dtype == np.float32 and bt.kblk.dtype == np.float32
+
+
+def test_kv_cache_shapes_and_poison():
+    w = synth.Workload("t", nq=1, heads=2, dim=8, active=10, capacity=12, k=4, poison=True)
+    kc, vc = synth.make_kv(w)
+    assert kc.shape == vc.shape == (48, 2, 8) and kc.dtype == np.float32
+    assert np.all(np.isfinite(kc[:40])) and np.all(np.isnan(kc[40:])) and np.all(np.isnan(vc[40:]))
+    assert not np.array_equal(kc[:40], vc[:40])
+    k2, v2 = synth.make_kv(w)
+    assert np.array_equal(kc[:40], k2[:40]) and np.array_equal(vc[:40], v2[:40])
+
+
+def test_int8_pool():
+    codes, scales = synth.make_pool_i8(40, 32, 2, 16, seed=3)
+    assert codes.shape == (40, 2, 16) and codes.dtype == np.int8
+    assert scales.shape == (40, 2) and scales.dtype == np.uint16
+    assert codes.min() >= -127 and codes.max() <= 127 and np.all(codes[32:] == 0)
+    s = scales.view(np.float16).astype(np.float64)
+    assert np.all((s[:32] >= 0.0099) & (s[:32] <= 0.0401)) and np.all(np.isnan(s[32:]))
+    c2, s2 = synth.make_pool_i8(40, 32, 2, 16, seed=3)
+    assert np.array_equal(codes, c2) and np.array_equal(scales, s2)
