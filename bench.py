@@ -30,6 +30,17 @@ fp32-equivalent rate beside it; or HBM for the few-query dot-product kernel
 
 The CPU baseline is the CPU oracle (FP64 scores, then a sort-based top-k of its
 fp32-rounded scores) timed on this host's cores over the same workload.
+
+With --attention (decode workloads, at most 8 queries) a step is the decode
+layer's whole QSA stage: the selection above, then qsa_sparse_decode_attention
+of the same queries over the cells of the selected blocks in a synthetic fp32
+key/value cache of the workload's capacity (4 cells per block, rotated over the
+same input copies).  `roofline_attention` then reports that call against HBM:
+its algorithmic bytes are the gathered key and value rows (2 * nq * k * 4 cells
+* heads * dim * 4 B) plus the queries, ids and outputs, over the event-timed
+duration of the call (both of its kernels and the gap between them).  --graph
+adds a pass that replays the steps from one captured HIP graph, which shows the
+GPU time per step without the per-call host cost of the Python binding.
 """
 from __future__ import annotations
 
@@ -76,6 +87,10 @@ def parse_args():
                    help="precision mode of qsa_block_scores_ex (auto = the library default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-threads", type=int, default=16)
+    p.add_argument("--attention", action="store_true",
+                   help="decode workloads: select, then attend over the selected blocks")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the steps replayed from one captured HIP graph")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -108,8 +123,9 @@ def read_traffic(path: str, workload: str):
         return None
 
 
-def cpu_baseline(w: synth.Workload, bt: synth.Batch, threads: int):
-    """Time the CPU oracle on all queries of the workload, `passes` times."""
+def cpu_baseline(w: synth.Workload, bt: synth.Batch, threads: int, kv=None):
+    """Time the CPU oracle on all queries of the workload, `passes` times (with
+    `kv` = (keys, values): the oracle's attention over its own selection too)."""
     import oracle
 
     orc = oracle.default()
@@ -121,7 +137,10 @@ def cpu_baseline(w: synth.Workload, bt: synth.Batch, threads: int):
         if len(rows) == 0:
             return
         s64 = orc.scores_f64(bt.q[rows], bt.kblk, w.active)
-        orc.topk(s64.astype(np.float32), w.k)
+        ids = orc.topk(s64.astype(np.float32), w.k)
+        if kv is not None:
+            orc.sparse_decode_attn_f64(bt.q[rows], kv[0], kv[1], ids, 4 * w.active,
+                                       1.0 / np.sqrt(w.dim))
 
     passes, rates = 3, []
     with cf.ThreadPoolExecutor(threads) as ex:
@@ -136,9 +155,47 @@ def cpu_baseline(w: synth.Workload, bt: synth.Batch, threads: int):
         "cores": threads,
         "kind": "oracle",
         "sample": (f"all {w.nq} queries x {w.active} blocks of {w.name} (FP64 scores + sort "
-                   f"top-k of the fp32-rounded scores), {passes} passes, median; "
-                   f"{threads} threads over query rows"),
+                   f"top-k of the fp32-rounded scores"
+                   + (", then FP64 attention over the selected blocks' cells" if kv else "")
+                   + f"), {passes} passes, median; {threads} threads over query rows"),
     }
+
+
+def graph_pass(torch, step, ncopy, K, outputs):
+    """Capture one step per input copy into a HIP graph on a side stream (after
+    warming the library's per-stream scratch there), replay it to cover K
+    steps, and check that every replay leaves the outputs of the eager steps."""
+    ref = [[t.clone() for t in group] for group in outputs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in range(ncopy):
+            step(c)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for c in range(ncopy):
+            step(c)
+    torch.cuda.synchronize()
+    reps = max(1, K // ncopy)
+    match = True
+    for _ in range(3):  # replays checked one by one, eager work between them
+        for group in outputs:
+            for t in group:
+                t.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        match = match and all(torch.equal(a, b) for ga, gb in zip(outputs, ref)
+                              for a, b in zip(ga, gb))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return {"ms_per_step": round(e0.elapsed_time(e1) / (reps * ncopy), 5), "match": bool(match)}
 
 
 def main():
@@ -153,7 +210,7 @@ def main():
     import torch
 
     from sparse_attention_kv_qsa_amd import (binding, qsa_block_scores_ex, qsa_block_select,
-                                             qsa_block_topk)
+                                             qsa_block_topk, qsa_sparse_decode_attention)
 
     binding.load_library()
     dev = torch.device("cuda:0")
@@ -176,16 +233,36 @@ def main():
     k_d = [torch.from_numpy(bt.kblk).to(dev) for _ in range(ncopy)]
     s_d = [torch.empty((w.nq, w.active), dtype=torch.float32, device=dev) for _ in range(ncopy)]
     i_d = [torch.empty((w.nq, w.k), dtype=torch.int32, device=dev) for _ in range(ncopy)]
+    attn = args.attention
+    if attn and w.nq > 8:
+        print(json.dumps({"error": "--attention times the decode layer: workloads of at most "
+                          "8 queries", "workload": w.name}))
+        sys.exit(2)
+    n_cells = 4 * w.active
+    if attn:
+        kv = synth.make_kv(w)
+        kc_d = [torch.from_numpy(kv[0]).to(dev) for _ in range(ncopy)]
+        vc_d = [torch.from_numpy(kv[1]).to(dev) for _ in range(ncopy)]
+        o_d = [torch.empty((w.nq, w.heads, w.dim), dtype=torch.float32, device=dev)
+               for _ in range(ncopy)]
     torch.cuda.synchronize()
 
     mode = args.scores_mode
 
-    def step(c):
+    def select(c):
         if mode == "auto":
             qsa_block_select(q_d[c], k_d[c], w.k, w.active, scores=s_d[c], ids=i_d[c])
         else:
             qsa_block_scores_ex(q_d[c], k_d[c], w.active, scores=s_d[c], mode=mode)
             qsa_block_topk(s_d[c], w.k, ids=i_d[c])
+
+    def attend(c):
+        qsa_sparse_decode_attention(q_d[c], kc_d[c], vc_d[c], i_d[c], n_cells, out=o_d[c])
+
+    def step(c):
+        select(c)
+        if attn:
+            attend(c)
 
     for it in range(args.warmup):
         step(it % ncopy)
@@ -220,6 +297,24 @@ def main():
     torch.cuda.synchronize()
     score_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
     topk_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+
+    attn_ms = None
+    if attn:
+        # Pass 2b: the attention call alone, events around each call (the ids
+        # of every copy were written by the passes above).
+        ea = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        torch.cuda.synchronize()
+        for it in range(K):
+            ea[it][0].record()
+            attend(it % ncopy)
+            ea[it][1].record()
+        torch.cuda.synchronize()
+        attn_ms = [ea[i][0].elapsed_time(ea[i][1]) for i in range(K)]
+
+    graph = None
+    if args.graph:
+        graph = graph_pass(torch, step, ncopy, K,
+                           [i_d] + ([o_d] if attn else []))
 
     flop = 2.0 * w.nq * w.active * w.K  # fp32-equivalent FLOP of the scores
     score_avg_s = float(np.mean(score_ms)) * 1e-3
@@ -292,8 +387,32 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if graph is not None:
+        out["stages"]["graph_ms_per_step"] = graph["ms_per_step"]
+        out["stages"]["graph_replays_match_eager"] = graph["match"]
+    if attn:
+        # Algorithmic bytes of one attention call: the gathered key and value
+        # rows, the queries, the ids and the outputs.
+        gathered = 2.0 * w.nq * w.k * 4 * w.K * 4
+        abytes = gathered + 4.0 * (2 * w.nq * w.K + w.nq * w.k)
+        a_avg_s = float(np.mean(attn_ms)) * 1e-3
+        gbs = abytes / a_avg_s / 1e9
+        out["metric"] = ("QSA decode layer: select + block-sparse attention over the "
+                         "selected blocks; queries*blocks/s")
+        out["vs_baseline"] = None
+        out["config"]["step"] += " + qsa_sparse_decode_attention"
+        out["config"]["kv_cells"] = 4 * w.capacity
+        out["config"]["attended_cells"] = 4 * w.k
+        out["data"] += "; N(0,1) fp32 key/value cells, NaN past the active blocks"
+        out["stages"]["attention_ms"] = round(float(np.mean(attn_ms)), 5)
+        out["stages"]["attention_ms_median"] = round(float(np.median(attn_ms)), 5)
+        out["roofline_attention"] = {
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+            "bytes_per_call": int(abytes),
+            "kernel": "attn_chunk_kernel + attn_merge_kernel (one call)"}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, bt, args.cpu_threads)
+        out["cpu_baseline"] = cpu_baseline(w, bt, args.cpu_threads, kv if attn else None)
     print(json.dumps(out), flush=True)
 
 
