@@ -37,7 +37,8 @@ of the same queries over the cells of the selected blocks in a synthetic fp32
 key/value cache of the workload's capacity (4 cells per block, rotated over the
 same input copies).  `roofline_attention` then reports that call against HBM:
 its algorithmic bytes are the gathered key and value rows (2 * nq * k * 4 cells
-* heads * dim * 4 B) plus the queries, ids and outputs, over the event-timed
+* heads * dim * 4 B; with --pool int8, dim one-byte codes and a 2-byte scale
+per cell and head) plus the queries, ids and outputs, over the event-timed
 duration of the call (both of its kernels and the gap between them).  --graph
 adds a pass that replays the steps from one captured HIP graph, which shows the
 GPU time per step without the per-call host cost of the Python binding.
@@ -89,6 +90,9 @@ def parse_args():
     p.add_argument("--cpu-threads", type=int, default=16)
     p.add_argument("--attention", action="store_true",
                    help="decode workloads: select, then attend over the selected blocks")
+    p.add_argument("--pool", default="fp32", choices=["fp32", "int8"],
+                   help="--attention: key/value cells as fp32 rows, or int8 codes with one "
+                        "binary16 scale per cell and head")
     p.add_argument("--graph", action="store_true",
                    help="also time the steps replayed from one captured HIP graph")
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -138,7 +142,10 @@ def cpu_baseline(w: synth.Workload, bt: synth.Batch, threads: int, kv=None):
             return
         s64 = orc.scores_f64(bt.q[rows], bt.kblk, w.active)
         ids = orc.topk(s64.astype(np.float32), w.k)
-        if kv is not None:
+        if kv is not None and len(kv) == 4:
+            orc.sparse_decode_attn_i8_f64(bt.q[rows], *kv, ids, 4 * w.active,
+                                          1.0 / np.sqrt(w.dim))
+        elif kv is not None:
             orc.sparse_decode_attn_f64(bt.q[rows], kv[0], kv[1], ids, 4 * w.active,
                                        1.0 / np.sqrt(w.dim))
 
@@ -210,7 +217,8 @@ def main():
     import torch
 
     from sparse_attention_kv_qsa_amd import (binding, qsa_block_scores_ex, qsa_block_select,
-                                             qsa_block_topk, qsa_sparse_decode_attention)
+                                             qsa_block_topk, qsa_sparse_decode_attention,
+                                             qsa_sparse_decode_attention_i8)
 
     binding.load_library()
     dev = torch.device("cuda:0")
@@ -239,10 +247,18 @@ def main():
                           "8 queries", "workload": w.name}))
         sys.exit(2)
     n_cells = 4 * w.active
-    if attn:
+    int8 = args.pool == "int8"
+    if attn and not int8:
         kv = synth.make_kv(w)
         kc_d = [torch.from_numpy(kv[0]).to(dev) for _ in range(ncopy)]
         vc_d = [torch.from_numpy(kv[1]).to(dev) for _ in range(ncopy)]
+    if attn and int8:
+        kq, ks = synth.make_pool_i8(4 * w.capacity, n_cells, w.heads, w.dim, seed=w.seed + 1)
+        vq, vs = synth.make_pool_i8(4 * w.capacity, n_cells, w.heads, w.dim, seed=w.seed + 2)
+        kv = (kq, ks, vq, vs)
+        pools = [tuple(torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+                       for a in kv) for _ in range(ncopy)]
+    if attn:
         o_d = [torch.empty((w.nq, w.heads, w.dim), dtype=torch.float32, device=dev)
                for _ in range(ncopy)]
     torch.cuda.synchronize()
@@ -257,7 +273,10 @@ def main():
             qsa_block_topk(s_d[c], w.k, ids=i_d[c])
 
     def attend(c):
-        qsa_sparse_decode_attention(q_d[c], kc_d[c], vc_d[c], i_d[c], n_cells, out=o_d[c])
+        if int8:
+            qsa_sparse_decode_attention_i8(q_d[c], *pools[c], i_d[c], n_cells, out=o_d[c])
+        else:
+            qsa_sparse_decode_attention(q_d[c], kc_d[c], vc_d[c], i_d[c], n_cells, out=o_d[c])
 
     def step(c):
         select(c)
@@ -393,7 +412,8 @@ def main():
     if attn:
         # Algorithmic bytes of one attention call: the gathered key and value
         # rows, the queries, the ids and the outputs.
-        gathered = 2.0 * w.nq * w.k * 4 * w.K * 4
+        gathered = (2.0 * w.nq * w.k * 4 * (w.K + 2 * w.heads) if int8 else
+                    2.0 * w.nq * w.k * 4 * w.K * 4)
         abytes = gathered + 4.0 * (2 * w.nq * w.K + w.nq * w.k)
         a_avg_s = float(np.mean(attn_ms)) * 1e-3
         gbs = abytes / a_avg_s / 1e9
@@ -403,14 +423,18 @@ def main():
         out["config"]["step"] += " + qsa_sparse_decode_attention"
         out["config"]["kv_cells"] = 4 * w.capacity
         out["config"]["attended_cells"] = 4 * w.k
-        out["data"] += "; N(0,1) fp32 key/value cells, NaN past the active blocks"
+        out["config"]["kv_pool"] = args.pool
+        out["data"] += ("; int8 key/value codes round(N(0,40)) with binary16 scales in "
+                        "[0.01, 0.04], NaN scales past the active blocks" if int8 else
+                        "; N(0,1) fp32 key/value cells, NaN past the active blocks")
         out["stages"]["attention_ms"] = round(float(np.mean(attn_ms)), 5)
         out["stages"]["attention_ms_median"] = round(float(np.median(attn_ms)), 5)
         out["roofline_attention"] = {
             "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
             "bytes_per_call": int(abytes),
-            "kernel": "attn_chunk_kernel + attn_merge_kernel (one call)"}
+            "kernel": ("attn_chunk_i8_kernel" if int8 else "attn_chunk_kernel")
+            + " + attn_merge_kernel (one call)"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, bt, args.cpu_threads, kv if attn else None)
     print(json.dumps(out), flush=True)

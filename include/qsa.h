@@ -45,6 +45,8 @@
 #ifndef QSA_H
 #define QSA_H
 
+#include <stdint.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -182,14 +184,44 @@ int qsa_block_select(const float *q, const float *kblk, int nq, int heads, int d
  * dim must be a multiple of 4 in [4, QSA_ATTN_MAX_DIM], heads*dim at most
  * QSA_MAX_HEAD_DIM and nq at most 65535 (else QSA_ERR_SHAPE); k in [0, QSA_TOPK_MAX_K] (else
  * QSA_ERR_K).  The cells are processed in fixed chunks of 8 listed blocks and
- * merged in chunk order, so results are deterministic; the error against an
- * FP64 evaluation stays within 1e-5 * max|v| of the attended cells.
+ * merged in chunk order, so results are deterministic.  Against an FP64
+ * evaluation the error of out[i][h][d] stays within
+ *   max|v| * (4e-6 + 24 * 2^-24 * |scale| * max_c sum_d |q[i][h][d] k[c][h][d]|)
+ * over the attended cells c (fp32 rounding of the dot products, of which the
+ * second term bounds the effect on the softmax weights).
  * nq == 0 or heads == 0 is a successful no-op.
  */
 #define QSA_ATTN_MAX_DIM 128
 int qsa_sparse_decode_attention(const float *q, const float *kcache, const float *vcache,
                                 const int *ids, int nq, int heads, int dim, int k, int n_cells,
                                 float scale, float *out, void *stream);
+
+/*
+ * qsa_sparse_decode_attention_i8 -- the same attention over an int8 key/value
+ * pool (the int8 pool of the decode-attention table on the page above; page
+ * "#3224 [Engine] perf(hip): tune RDNA4 QSA prompt WMMA path
+ * (STRATA_HIP_WMMA stays opt-in)", Summary item 2: int8 keys and values with
+ * FP16 scales).  A key element stands for kcode[c][h][d] * kscale[c][h], a
+ * value element for vcode[c][h][d] * vscale[c][h]:
+ *
+ *   kcode    [>= n_cells][heads][dim] int8 codes, 16-byte aligned; vcode the
+ *   vcode    same for values.
+ *   kscale   [>= n_cells][heads] IEEE binary16 scales (bit patterns), 2-byte
+ *   vscale   aligned.
+ *   q, ids, n_cells, scale, out, stream: as for qsa_sparse_decode_attention,
+ *            whose formula this computes on the dequantised rows.
+ *
+ * dim must be a multiple of 16 in [16, QSA_ATTN_MAX_DIM] (else
+ * QSA_ERR_SHAPE); other limits and errors as above.  The kernel forms
+ * scale * (kscale * sum_d q_d kcode_d) and sums (w * vscale) * vcode in fp32;
+ * against an FP64 evaluation on the dequantised rows the error stays within
+ *   max|v| * (8e-6 + 48 * 2^-24 * |scale| * max_c sum_d |q[i][h][d] k[c][h][d]|).
+ * A cell costs 2 * (dim + 2) bytes per head to read instead of 8 * dim.
+ */
+int qsa_sparse_decode_attention_i8(const float *q, const int8_t *kcode, const uint16_t *kscale,
+                                   const int8_t *vcode, const uint16_t *vscale, const int *ids,
+                                   int nq, int heads, int dim, int k, int n_cells, float scale,
+                                   float *out, void *stream);
 
 /* Human-readable text of a status code (a static string; never NULL). */
 const char *qsa_strerror(int status);

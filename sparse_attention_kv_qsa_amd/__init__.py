@@ -2,13 +2,15 @@
 
 The compute lives in ``libqsa.so`` (hand-written HIP for CDNA4, C ABI declared
 in ``include/qsa.h``).  ``qsa_block_scores`` / ``qsa_block_topk`` /
-``qsa_block_select`` / ``qsa_sparse_decode_attention`` here are thin ctypes
+``qsa_block_select`` / ``qsa_sparse_decode_attention`` (and ``_i8``, over an
+int8 key/value pool) here are thin ctypes
 bindings with the same names as the C entry points: they marshal torch
 tensors and the current HIP stream, nothing more.  There is no CPU fallback:
 calling them without the built library, or with tensors that are not on the
 GPU, raises.
 """
-from .synth import WORKLOADS, HEADLINE, Workload, make_batch, make_random, fingerprint  # noqa: F401
+from .synth import (WORKLOADS, HEADLINE, Workload, make_batch, make_random, make_kv,  # noqa: F401
+                    make_pool_i8, fingerprint)
 
 
 def __getattr__(name):
@@ -16,6 +18,7 @@ def __getattr__(name):
     # generator can be imported on hosts without the library.
     if name in ("qsa_block_scores", "qsa_block_scores_ex", "qsa_block_topk", "qsa_block_select",
                 "qsa_sparse_decode_attention", "sparse_decode_attention", "QSA_ATTN_MAX_DIM",
+                "qsa_sparse_decode_attention_i8", "sparse_decode_attention_i8",
                 "qsa_strerror", "TOPK_FEW_ROWS",
                 "QSAError", "SCORE_MODES",
                 "load_library", "library_path", "TOPK_MAX_K", "block_scores", "block_topk"):

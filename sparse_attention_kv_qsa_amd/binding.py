@@ -36,6 +36,8 @@ SIGNATURES = {
     "qsa_block_select": (_I, [_VP, _VP, _I, _I, _I, _I, _I, _VP, _VP, _VP]),
     "qsa_sparse_decode_attention": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_float,
                                          _VP, _VP]),
+    "qsa_sparse_decode_attention_i8": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I,
+                                            ctypes.c_float, _VP, _VP]),
     "qsa_strerror": (ctypes.c_char_p, [_I]),
 }
 
@@ -210,7 +212,53 @@ def qsa_sparse_decode_attention(q: torch.Tensor, kcache: torch.Tensor, vcache: t
     return out
 
 
+def qsa_sparse_decode_attention_i8(q: torch.Tensor, kcode: torch.Tensor, kscale: torch.Tensor,
+                                   vcode: torch.Tensor, vscale: torch.Tensor, ids: torch.Tensor,
+                                   n_cells: int | None = None, scale: float | None = None,
+                                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """qsa_sparse_decode_attention over an int8 pool: kcode/vcode [cells, heads,
+    dim] int8 codes, kscale/vscale [cells, heads] binary16 scales (float16, or
+    int16 bit patterns); an element stands for code * scale."""
+    _require_gpu_f32("q", q, 3)
+    nq, heads, dim = q.shape
+    for name, t in (("kcode", kcode), ("vcode", vcode)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int8 or t.dim() != 3 or \
+                not t.is_contiguous() or t.device != q.device or t.shape[1:] != (heads, dim):
+            raise ValueError(f"{name} must be a contiguous int8 [cells, {heads}, {dim}] tensor "
+                             "on q's device")
+    cells = kcode.shape[0]
+    if vcode.shape[0] != cells:
+        raise ValueError("kcode and vcode must have the same number of cells")
+    for name, t in (("kscale", kscale), ("vscale", vscale)):
+        if not isinstance(t, torch.Tensor) or t.dtype not in (torch.float16, torch.int16) or \
+                tuple(t.shape) != (cells, heads) or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous float16 (or int16 bits) "
+                             f"[{cells}, {heads}] tensor on q's device")
+    n = cells if n_cells is None else int(n_cells)
+    if not 0 <= n <= cells:
+        raise ValueError(f"n_cells={n} outside [0, {cells}]")
+    if ids.dtype != torch.int32 or ids.dim() != 2 or ids.shape[0] != nq or \
+            not ids.is_contiguous() or ids.device != q.device:
+        raise ValueError(f"ids must be a contiguous int32 [{nq}, k] tensor on q's device")
+    k = ids.shape[1]
+    sc = 1.0 / float(dim) ** 0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((nq, heads, dim), dtype=torch.float32, device=q.device)
+    elif tuple(out.shape) != (nq, heads, dim) or out.dtype != torch.float32 or \
+            not out.is_contiguous() or out.device != q.device:
+        raise ValueError(f"out must be a contiguous float32 [{nq}, {heads}, {dim}] tensor on q's device")
+    with torch.cuda.device(q.device):
+        st = load_library().qsa_sparse_decode_attention_i8(
+            q.data_ptr(), kcode.data_ptr(), kscale.data_ptr(), vcode.data_ptr(),
+            vscale.data_ptr(), ids.data_ptr() if ids.numel() else None, nq, heads, dim, k, n, sc,
+            out.data_ptr(), _stream_handle(q.device))
+    if st != QSA_OK:
+        raise QSAError(st, "qsa_sparse_decode_attention_i8")
+    return out
+
+
 # Short aliases.
 block_scores = qsa_block_scores
 block_topk = qsa_block_topk
 sparse_decode_attention = qsa_sparse_decode_attention
+sparse_decode_attention_i8 = qsa_sparse_decode_attention_i8

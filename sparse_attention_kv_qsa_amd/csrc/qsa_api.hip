@@ -99,6 +99,28 @@ extern "C" int qsa_sparse_decode_attention(const float *q, const float *kcache, 
                                                            static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int qsa_sparse_decode_attention_i8(const float *q, const int8_t *kcode,
+                                              const uint16_t *kscale, const int8_t *vcode,
+                                              const uint16_t *vscale, const int *ids, int nq,
+                                              int heads, int dim, int k, int n_cells, float scale,
+                                              float *out, void *stream) {
+  if (nq < 0 || heads < 0 || dim < 0 || n_cells < 0) return QSA_ERR_SHAPE;
+  if (!qsa::attn_i8_dim_ok(dim) || int64_t(heads) * dim > QSA_MAX_HEAD_DIM) return QSA_ERR_SHAPE;
+  if (nq > 65535) return QSA_ERR_SHAPE;
+  if (k < 0 || k > QSA_TOPK_MAX_K) return QSA_ERR_K;
+  if (nq == 0 || heads == 0) return QSA_OK;
+  if (!q || !out || (k > 0 && !ids) ||
+      (n_cells > 0 && (!kcode || !kscale || !vcode || !vscale)))
+    return QSA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(kcode, 16) || !aligned(vcode, 16) || !aligned(kscale, 2) ||
+      !aligned(vscale, 2) || !aligned(ids, 4) || !aligned(out, 4))
+    return QSA_ERR_ALIGN;
+  (void)hipGetLastError();
+  return launch_status(qsa::launch_sparse_decode_attention_i8(
+      q, kcode, kscale, vcode, vscale, ids, nq, heads, dim, k, n_cells, scale, out,
+      static_cast<hipStream_t>(stream)));
+}
+
 extern "C" const char *qsa_strerror(int status) {
   switch (status) {
     case QSA_OK:
@@ -107,7 +129,7 @@ extern "C" const char *qsa_strerror(int status) {
       return "a required pointer is NULL";
     case QSA_ERR_SHAPE:
       return "bad shape: a size is negative, heads*dim is not a multiple of 4 in [4, 4096], "
-             "or an attention dim is not a multiple of 4 in [4, 128]";
+             "or an attention dim is not a multiple of 4 (int8 pool: 16) in [4 (16), 128]";
     case QSA_ERR_K:
       return "bad k: k < 0 or k > 4096";
     case QSA_ERR_ALIGN:

@@ -27,6 +27,16 @@
 //      every wave needs writes back its XCD's L2.
 // Bound: HBM (the gathered key and value rows); the fixed chunking and merge
 // order make the result deterministic.
+//
+// An int8 pool (the int8 rows of that page's decode-attention table; page
+// "#3224 [Engine] perf(hip): tune RDNA4 QSA prompt WMMA path (STRATA_HIP_WMMA
+// stays opt-in)", Summary item 2: int8 keys and values carry FP16 scales)
+// holds one signed code per (cell, head, d) and one binary16 scale per
+// (cell, head).  attn_chunk_i8_kernel gathers 16 codes per lane (a row of dim
+// codes over dim/16 lanes), forms the dot product of q with the codes and
+// multiplies by the key scale once per cell, and accumulates (w * value scale)
+// * code; the partials and the merge are those of the fp32 pool.  A cell then
+// costs 2 * (dim + 2) bytes per head instead of 8 * dim.
 #include <hip/hip_runtime.h>
 
 #include "qsa_device.h"
@@ -163,6 +173,128 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(const float *__restrict_
   if (grp == 0 && live) *reinterpret_cast<f4 *>(dst + 4 + 4 * sub) = acc;
 }
 
+// The int8 pool.  LPC lanes hold one cell's row of dim codes, 16 each (LPC =
+// dim/16 rounded up to a power of two, dim <= 128), so one load instruction
+// covers 64/LPC cells; the scales are one 2-byte load per cell (all LPC lanes
+// of a cell read the same address).
+template <int LPC>
+__global__ __launch_bounds__(64) void attn_chunk_i8_kernel(
+    const float *__restrict__ q, const int8_t *__restrict__ kq, const uint16_t *__restrict__ ks,
+    const int8_t *__restrict__ vq, const uint16_t *__restrict__ vs, const int *__restrict__ ids,
+    int heads, int dim, int k, int n_cells, float scale, float *__restrict__ part, int nchunks) {
+  constexpr int CPI = 64 / LPC;
+  constexpr int ROUNDS = kChunkCells / CPI > 0 ? kChunkCells / CPI : 1;
+  const int lane = threadIdx.x;
+  const int chunk = blockIdx.x;
+  const int h = blockIdx.y;
+  const int i = blockIdx.z;
+  const int sub = lane & (LPC - 1);
+  const int grp = lane / LPC;
+  const bool live = 16 * sub < dim;
+
+  const int j0 = chunk * kChunkBlocks;
+  int my_id = -1;
+  if (lane < kChunkBlocks && j0 + lane < k) my_id = ids[int64_t(i) * k + j0 + lane];
+
+  const int64_t row = int64_t(heads) * dim;  // codes per cell
+  const int64_t col = int64_t(h) * dim + 16 * sub;
+
+  int64_t cell[ROUNDS];
+  bool ok[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int slot = r * CPI + grp;
+    const int b = __shfl(my_id, (slot >> 2) & 63, 64);
+    const int64_t c = int64_t(b) * 4 + (slot & 3);
+    ok[r] = slot < kChunkCells && b >= 0 && c < n_cells;
+    cell[r] = c;
+  }
+  uint4 kv[ROUNDS], vv[ROUNDS];
+  uint16_t ksc[ROUNDS], vsc[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    kv[r] = uint4{0u, 0u, 0u, 0u};
+    ksc[r] = 0;
+    if (ok[r]) {
+      if (live) kv[r] = *reinterpret_cast<const uint4 *>(kq + cell[r] * row + col);
+      ksc[r] = ks[cell[r] * heads + h];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    vv[r] = uint4{0u, 0u, 0u, 0u};
+    vsc[r] = 0;
+    if (ok[r]) {
+      if (live) vv[r] = *reinterpret_cast<const uint4 *>(vq + cell[r] * row + col);
+      vsc[r] = vs[cell[r] * heads + h];
+    }
+  }
+  float qv[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) qv[e] = 0.f;
+  if (live) {
+    const f4 *qp = reinterpret_cast<const f4 *>(q + (int64_t(i) * heads + h) * dim + 16 * sub);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f4 t = qp[e];
+      qv[4 * e] = t.x;
+      qv[4 * e + 1] = t.y;
+      qv[4 * e + 2] = t.z;
+      qv[4 * e + 3] = t.w;
+    }
+  }
+
+  // Signed byte e of a row of 16 codes, as a float.
+  auto code = [](const uint4 &u, int e) {
+    const uint32_t wv = e < 4 ? u.x : e < 8 ? u.y : e < 12 ? u.z : u.w;
+    return float(int(int8_t(uint8_t(wv >> (8 * (e & 3))))));
+  };
+
+  float s[ROUNDS];
+  float m = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    float p = qv[0] * code(kv[r], 0);
+#pragma unroll
+    for (int e = 1; e < 16; ++e) p = __builtin_fmaf(qv[e], code(kv[r], e), p);
+    const float kscale = float(__builtin_bit_cast(_Float16, ksc[r]));
+    s[r] = ok[r] ? scale * (cell_sum<LPC>(p) * kscale) : -INFINITY;
+    m = fmaxf(m, s[r]);
+  }
+  m = group_all<LPC>(m, [](float a, float b) { return fmaxf(a, b); });
+
+  float l = 0.f;
+  float acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  if (m > -INFINITY) {
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      const float w = ok[r] ? expf(s[r] - m) : 0.f;
+      l += w;
+      const float wv = w * float(__builtin_bit_cast(_Float16, vsc[r]));
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = __builtin_fmaf(wv, code(vv[r], e), acc[e]);
+    }
+  }
+  auto add = [](float a, float b) { return a + b; };
+  l = group_all<LPC>(l, add);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = group_all<LPC>(acc[e], add);
+
+  float *dst = part + ((int64_t(i) * heads + h) * nchunks + chunk) * (dim + 4);
+  if (lane == 0) {
+    dst[0] = m;
+    dst[1] = l;
+  }
+  if (grp == 0 && live) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      *reinterpret_cast<f4 *>(dst + 4 + 16 * sub + 4 * e) =
+          f4{acc[4 * e], acc[4 * e + 1], acc[4 * e + 2], acc[4 * e + 3]};
+  }
+}
+
 // One workgroup of kMergeWaves waves per (query, head) folds the chunk
 // partials.  Wave w takes the w-th contiguous quarter of the chunks and issues
 // all of its loads at once; M = max m_j over all chunks, e_j = exp(m_j - M);
@@ -279,19 +411,47 @@ hipError_t launch_chunks(const float *q, const float *kc, const float *vc, const
   return hipGetLastError();
 }
 
+template <int LPC>
+hipError_t launch_chunks_i8(const float *q, const int8_t *kq, const uint16_t *ks,
+                            const int8_t *vq, const uint16_t *vs, const int *ids, int nq,
+                            int heads, int dim, int k, int n_cells, float scale, float *part,
+                            int nchunks, hipStream_t stream) {
+  attn_chunk_i8_kernel<LPC><<<dim3(nchunks, heads, nq), 64, 0, stream>>>(
+      q, kq, ks, vq, vs, ids, heads, dim, k, n_cells, scale, part, nchunks);
+  return hipGetLastError();
+}
+
+// Chunk partials of nq * heads * nchunks chunks from the stream's scratch.
+hipError_t chunk_partials(hipStream_t stream, int nq, int heads, int dim, int k, int *nchunks,
+                          float **part) {
+  *nchunks = k > 0 ? (k + kChunkBlocks - 1) / kChunkBlocks : 1;
+  void *ws = nullptr;
+  hipError_t e =
+      workspace(stream, size_t(nq) * heads * *nchunks * (dim + 4) * sizeof(float), &ws);
+  *part = static_cast<float *>(ws);
+  return e;
+}
+
+hipError_t launch_merge(const float *part, int nq, int heads, int dim, int nchunks, float *out,
+                        hipStream_t stream) {
+  attn_merge_kernel<<<dim3(heads, nq), 64 * kMergeWaves, 0, stream>>>(part, heads, dim, nchunks,
+                                                                      out);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool attn_dim_ok(int dim) { return dim >= 4 && dim % 4 == 0 && dim <= kAttnMaxDim; }
+bool attn_i8_dim_ok(int dim) { return dim >= 16 && dim % 16 == 0 && dim <= kAttnMaxDim; }
 
 hipError_t launch_sparse_decode_attention(const float *q, const float *kc, const float *vc,
                                           const int *ids, int nq, int heads, int dim, int k,
                                           int n_cells, float scale, float *out,
                                           hipStream_t stream) {
-  const int nchunks = k > 0 ? (k + kChunkBlocks - 1) / kChunkBlocks : 1;
-  void *ws = nullptr;
-  hipError_t e = workspace(stream, size_t(nq) * heads * nchunks * (dim + 4) * sizeof(float), &ws);
+  int nchunks = 0;
+  float *part = nullptr;
+  hipError_t e = chunk_partials(stream, nq, heads, dim, k, &nchunks, &part);
   if (e != hipSuccess) return e;
-  float *part = static_cast<float *>(ws);
   const int lpc = dim <= 4 ? 1 : dim <= 8 ? 2 : dim <= 16 ? 4 : dim <= 32 ? 8 : dim <= 64 ? 16 : 32;
   switch (lpc) {
     case 1: e = launch_chunks<1>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
@@ -302,8 +462,27 @@ hipError_t launch_sparse_decode_attention(const float *q, const float *kc, const
     default: e = launch_chunks<32>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
   }
   if (e != hipSuccess) return e;
-  attn_merge_kernel<<<dim3(heads, nq), 64 * kMergeWaves, 0, stream>>>(part, heads, dim, nchunks, out);
-  return hipGetLastError();
+  return launch_merge(part, nq, heads, dim, nchunks, out, stream);
+}
+
+hipError_t launch_sparse_decode_attention_i8(const float *q, const int8_t *kq,
+                                             const uint16_t *ks, const int8_t *vq,
+                                             const uint16_t *vs, const int *ids, int nq,
+                                             int heads, int dim, int k, int n_cells,
+                                             float scale, float *out, hipStream_t stream) {
+  int nchunks = 0;
+  float *part = nullptr;
+  hipError_t e = chunk_partials(stream, nq, heads, dim, k, &nchunks, &part);
+  if (e != hipSuccess) return e;
+  const int lpc = dim <= 16 ? 1 : dim <= 32 ? 2 : dim <= 64 ? 4 : 8;
+  switch (lpc) {
+    case 1: e = launch_chunks_i8<1>(q, kq, ks, vq, vs, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
+    case 2: e = launch_chunks_i8<2>(q, kq, ks, vq, vs, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
+    case 4: e = launch_chunks_i8<4>(q, kq, ks, vq, vs, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
+    default: e = launch_chunks_i8<8>(q, kq, ks, vq, vs, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
+  }
+  if (e != hipSuccess) return e;
+  return launch_merge(part, nq, heads, dim, nchunks, out, stream);
 }
 
 }  // namespace qsa

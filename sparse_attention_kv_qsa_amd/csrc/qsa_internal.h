@@ -72,5 +72,14 @@ hipError_t launch_sparse_decode_attention(const float *q, const float *kc, const
                                           const int *ids, int nq, int heads, int dim, int k,
                                           int n_cells, float scale, float *out,
                                           hipStream_t stream);
+// The same over an int8 pool: codes kq/vq[cells][heads][dim] int8, one
+// binary16 scale per (cell, head) in ks/vs[cells][heads]; an element stands
+// for code * scale.  dim in [16, kAttnMaxDim], a multiple of 16.
+bool attn_i8_dim_ok(int dim);
+hipError_t launch_sparse_decode_attention_i8(const float *q, const int8_t *kq,
+                                             const uint16_t *ks, const int8_t *vq,
+                                             const uint16_t *vs, const int *ids, int nq,
+                                             int heads, int dim, int k, int n_cells,
+                                             float scale, float *out, hipStream_t stream);
 
 }  // namespace qsa

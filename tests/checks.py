@@ -29,9 +29,16 @@ import numpy as np
 # bounded by ATTN_TOL = 4e-6 at the sizes tested.
 ATTN_TOL = 4e-6
 ATTN_SCORE_TOL = 2 * 12 * 2.0 ** -24
+# The int8 pool, gated on its dequantised rows: a lane's score sums 16
+# code products in one FMA chain, then a lane tree of <= 3 levels and two
+# multiplications (key scale, then scale): <= 21 roundings, 24 with margin,
+# doubled as above.  The value sums take one more rounding per term (w times
+# the value scale): ATTN_I8_TOL = 2 * ATTN_TOL.
+ATTN_I8_TOL = 8e-6
+ATTN_I8_SCORE_TOL = 2 * 24 * 2.0 ** -24
 
 
-def attn_limit(q, kc, vc, ids, n_cells, scale):
+def attn_limit(q, kc, vc, ids, n_cells, scale, tol=ATTN_TOL, score_tol=ATTN_SCORE_TOL):
     """The gate above for every (query, head): an array [nq][heads]."""
     nq, heads, _ = q.shape
     lim = np.zeros((nq, heads))
@@ -41,7 +48,7 @@ def attn_limit(q, kc, vc, ids, n_cells, scale):
             continue
         vmax = np.abs(vc[cells].astype(np.float64)).max(axis=(0, 2))                  # [heads]
         qk = np.abs(q[i][None].astype(np.float64) * kc[cells].astype(np.float64)).sum(axis=2)
-        lim[i] = vmax * (ATTN_TOL + ATTN_SCORE_TOL * abs(scale) * qk.max(axis=0))
+        lim[i] = vmax * (tol + score_tol * abs(scale) * qk.max(axis=0))
     return lim
 
 

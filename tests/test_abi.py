@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "qsa.h")
 def header_entry_points() -> list[str]:
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(qsa_[a-z0-9_]+)\s*\(", text)))
 
 
 def header_macros() -> dict[str, int]:
@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert header_entry_points() == ["qsa_block_scores", "qsa_block_scores_ex", "qsa_block_select",
                                      "qsa_block_topk", "qsa_sparse_decode_attention",
-                                     "qsa_strerror"]
+                                     "qsa_sparse_decode_attention_i8", "qsa_strerror"]
 
 
 def test_binding_covers_the_header():
@@ -58,7 +58,7 @@ def test_binding_covers_the_header():
 def test_library_exports_every_declared_symbol(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
                          capture_output=True, text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (qsa_[a-z_]+)$", out, flags=re.M))
+    exported = set(re.findall(r"\bT (qsa_[a-z0-9_]+)$", out, flags=re.M))
     for name in header_entry_points():
         assert name in exported, name
         assert getattr(lib, name) is not None
@@ -171,6 +171,32 @@ def test_block_select_argument_checks(lib, args, status):
 ])
 def test_sparse_decode_attention_argument_checks(lib, args, status):
     assert lib.qsa_sparse_decode_attention(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    # q, kcode, kscale, vcode, vscale, ids, nq, heads, dim, k, n_cells, scale, out
+    ((P16, P16, P16, P16, P16, P16, -1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_SHAPE),
+    ((P16, P16, P16, P16, P16, P16, 1, 4, 120, 8, 100, 0.1, P16), binding.QSA_ERR_SHAPE),  # dim % 16
+    ((P16, P16, P16, P16, P16, P16, 1, 4, 8, 8, 100, 0.1, P16), binding.QSA_ERR_SHAPE),    # dim < 16
+    ((P16, P16, P16, P16, P16, P16, 1, 4, 144, 8, 100, 0.1, P16), binding.QSA_ERR_SHAPE),  # dim > 128
+    ((P16, P16, P16, P16, P16, P16, 1, 40, 128, 8, 100, 0.1, P16), binding.QSA_ERR_SHAPE),
+    ((P16, P16, P16, P16, P16, P16, 1, 4, 128, 8, -1, 0.1, P16), binding.QSA_ERR_SHAPE),
+    ((P16, P16, P16, P16, P16, P16, 1, 4, 128, 4097, 100, 0.1, P16), binding.QSA_ERR_K),
+    ((P16, P16, P16, P16, P16, P16, 1, 4, 128, -1, 100, 0.1, P16), binding.QSA_ERR_K),
+    ((P16, None, P16, P16, P16, P16, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_NULL),
+    ((P16, P16, None, P16, P16, P16, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_NULL),
+    ((P16, P16, P16, None, P16, P16, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_NULL),
+    ((P16, P16, P16, P16, None, P16, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_NULL),
+    ((P16, P16, P16, P16, P16, None, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_NULL),
+    ((P16, P16, P16, P16, P16, P16, 1, 4, 128, 8, 100, 0.1, None), binding.QSA_ERR_NULL),
+    ((P16, P16 + 8, P16, P16, P16, P16, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_ALIGN),
+    ((P16, P16, P16 + 1, P16, P16, P16, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_ALIGN),
+    ((P16, P16, P16, P16, P16 + 1, P16, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_ALIGN),
+    ((P16 + 4, P16, P16, P16, P16, P16, 1, 4, 128, 8, 100, 0.1, P16), binding.QSA_ERR_ALIGN),
+    ((None, None, None, None, None, None, 0, 4, 128, 8, 100, 0.1, None), binding.QSA_OK),
+])
+def test_sparse_decode_attention_i8_argument_checks(lib, args, status):
+    assert lib.qsa_sparse_decode_attention_i8(*args, None) == status
 
 
 def test_binding_refuses_cpu_tensors():

@@ -5,7 +5,9 @@ Gate, the same at every size: for every query i and head h,
     max_d |out_gpu[i][h][d] - out64[i][h][d]| <= attn_limit(...)[i][h]
 = max|v| of the attended cells x (4e-6 + 1.4e-6 x scale x max_c sum_d |q_d k_cd|)
 (tests/checks.py derives it from the fp32 arithmetic), bitwise where the exact
-result is an fp32 number (a single attended cell, no attended cell).  The attended cells of
+result is an fp32 number (a single attended cell, no attended cell).  The int8
+pool is gated the same way on its dequantised rows (code * binary16 scale,
+exact in fp32) with the int8 kernel's own constants (8e-6 and 48 * 2^-24).  The attended cells of
 a query are those of its listed blocks (4 per block) below n_cells.
 """
 from __future__ import annotations
@@ -16,7 +18,7 @@ import numpy as np
 import pytest
 
 import oracle
-from checks import attn_limit
+from checks import ATTN_I8_SCORE_TOL, ATTN_I8_TOL, attn_limit
 from sparse_attention_kv_qsa_amd import synth
 
 torch = pytest.importorskip("torch")
@@ -126,3 +128,98 @@ def test_attention_after_selection():
                               w.active)
     ids = ids.cpu().numpy()
     check_attn(bt.q, kc, vc, ids, n_cells, 1.0 / np.sqrt(w.dim))
+
+
+@pytest.mark.parametrize("name", ["decode-128k", "decode-128k-t4"])
+def test_attention_full_size_after_selection(name):
+    """The benchmarked decode layer at full size: a 262,152-cell fp32 cache, the
+    ids of the library's own selection, every output checked."""
+    from sparse_attention_kv_qsa_amd import qsa_block_select
+    w = synth.WORKLOADS[name]
+    bt = synth.make_batch(w)
+    kc, vc = synth.make_kv(w)
+    _, ids = qsa_block_select(torch.from_numpy(bt.q).cuda(), torch.from_numpy(bt.kblk).cuda(), w.k,
+                              w.active)
+    check_attn(bt.q, kc, vc, ids.cpu().numpy(), 4 * w.active, 1.0 / np.sqrt(w.dim))
+
+
+# ------------------------------------------------------------ int8 pool ----
+
+def dequantize(codes, scale_bits):
+    return codes.astype(np.float32) * scale_bits.view(np.float16).astype(np.float32)[..., None]
+
+
+def gpu_attn_i8(q, kq, ks, vq, vs, ids, n_cells, scale):
+    from sparse_attention_kv_qsa_amd import qsa_sparse_decode_attention_i8
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    out = qsa_sparse_decode_attention_i8(t(q), t(kq), t(ks.view(np.int16)), t(vq),
+                                         t(vs.view(np.int16)), t(ids.astype(np.int32)),
+                                         n_cells, scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_attn_i8(q, kq, ks, vq, vs, ids, n_cells, scale):
+    got = gpu_attn_i8(q, kq, ks, vq, vs, ids, n_cells, scale)
+    want = ORC.sparse_decode_attn_i8_f64(q, kq, ks, vq, vs, ids, n_cells, scale)
+    err = np.abs(got.astype(np.float64) - want).max(axis=2)
+    lim = attn_limit(q, dequantize(kq, ks), dequantize(vq, vs), ids, n_cells, scale,
+                     tol=ATTN_I8_TOL, score_tol=ATTN_I8_SCORE_TOL)
+    bad = np.argwhere(err > lim)
+    assert bad.size == 0, (f"{len(bad)} (query, head) pairs over the gate; first {tuple(bad[0])}: "
+                           f"error {err[tuple(bad[0])]:.3e} vs limit {lim[tuple(bad[0])]:.3e}")
+    return got
+
+
+def case_i8(seed, nq, heads, dim, n_cells, k, cap_extra=5, pad=0.0, dup=False, past=False):
+    q, _, _, ids = case(seed, nq, heads, dim, n_cells, k, cap_extra, pad, dup, past)
+    kq, ks = synth.make_pool_i8(n_cells + cap_extra, n_cells, heads, dim, seed=seed + 1)
+    vq, vs = synth.make_pool_i8(n_cells + cap_extra, n_cells, heads, dim, seed=seed + 2)
+    return q, kq, ks, vq, vs, ids  # scales past n_cells are NaN: never read
+
+
+SHAPES_I8 = [  # nq, heads, dim, n_cells, k
+    (1, 4, 128, 2048, 512), (1, 4, 128, 4001, 300), (4, 4, 128, 9000, 512), (1, 1, 16, 37, 9),
+    (3, 2, 32, 130, 13), (1, 3, 48, 99, 25), (2, 8, 64, 513, 8), (2, 2, 80, 300, 17),
+    (8, 4, 96, 600, 129), (1, 2, 112, 5, 1), (3, 4, 128, 257, 33),
+]
+
+
+@pytest.mark.parametrize("nq,heads,dim,n_cells,k", SHAPES_I8)
+def test_attention_i8_random(nq, heads, dim, n_cells, k):
+    q, kq, ks, vq, vs, ids = case_i8(nq * 37 + dim + k, nq, heads, dim, n_cells, k, pad=0.1,
+                                     dup=True, past=True)
+    check_attn_i8(q, kq, ks, vq, vs, ids, n_cells, 1.0 / np.sqrt(dim))
+
+
+def test_attention_i8_scales_extreme_codes():
+    q, kq, ks, vq, vs, ids = case_i8(9, 2, 4, 128, 800, 64)
+    kq[:800:3] = 127
+    vq[1:800:5] = -127
+    kq[2:800:7, :, ::2] = -128          # the one code without a positive twin
+    for scale in (0.0, 0.05, 1.0 / np.sqrt(128), 1.0):
+        check_attn_i8(q, kq, ks, vq, vs, ids, 800, scale)
+
+
+def test_attention_i8_single_cell_and_empty_are_exact():
+    q, kq, ks, vq, vs, _ = case_i8(10, 2, 3, 64, 41, 0)
+    vq[40, 1, :3] = [-128, 127, 0]
+    one = np.array([[10, -1], [-1, 10]], np.int32)
+    got = gpu_attn_i8(q, kq, ks, vq, vs, one, 41, 0.3)
+    want = dequantize(vq, vs)[40]
+    assert np.array_equal(got[0], want) and np.array_equal(got[1], want)
+    assert np.all(gpu_attn_i8(q, kq, ks, vq, vs, np.full((2, 4), -1, np.int32), 41, 0.3) == 0)
+
+
+def test_attention_i8_full_size_after_selection():
+    """decode-128k on an int8 pool of 262,152 cells: the library's selection,
+    then attention over it, every output checked."""
+    from sparse_attention_kv_qsa_amd import qsa_block_select
+    w = synth.WORKLOADS["decode-128k"]
+    bt = synth.make_batch(w)
+    cells = 4 * w.capacity
+    kq, ks = synth.make_pool_i8(cells, 4 * w.active, w.heads, w.dim, seed=11)
+    vq, vs = synth.make_pool_i8(cells, 4 * w.active, w.heads, w.dim, seed=12)
+    _, ids = qsa_block_select(torch.from_numpy(bt.q).cuda(), torch.from_numpy(bt.kblk).cuda(), w.k,
+                              w.active)
+    check_attn_i8(bt.q, kq, ks, vq, vs, ids.cpu().numpy(), 4 * w.active, 1.0 / np.sqrt(w.dim))
