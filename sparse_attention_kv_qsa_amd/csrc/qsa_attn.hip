@@ -20,11 +20,13 @@
 //      weighted value sum acc, and writes (m, l, acc[dim]).
 //   2. attn_merge_kernel: one workgroup per (query, head) folds the chunk
 //      partials: M = max m_j, L = sum l_j e^(m_j - M),
-//      out = sum acc_j e^(m_j - M) / L, in a fixed order (each of four waves
-//      sums a contiguous quarter of the chunks, then the four in order).
+//      out = sum acc_j e^(m_j - M) / L, in a fixed order (each wave sums 32
+//      consecutive chunks, then the waves' sums are added in order).
 //      A fused variant (the last chunk wave of a (query, head) merging, found
 //      by an atomic count) is slower on this GPU: the device-scope release
-//      every wave needs writes back its XCD's L2.
+//      every wave needs writes back its XCD's L2, and even with write-through
+//      partials and no fences the count's atomics serialise on one address
+//      (k = 4096: 512 waves per (query, head)).
 // Bound: HBM (the gathered key and value rows); the fixed chunking and merge
 // order make the result deterministic.
 //
@@ -295,95 +297,70 @@ __global__ __launch_bounds__(64) void attn_chunk_i8_kernel(
   }
 }
 
-// One workgroup of kMergeWaves waves per (query, head) folds the chunk
-// partials.  Wave w takes the w-th contiguous quarter of the chunks and issues
-// all of its loads at once; M = max m_j over all chunks, e_j = exp(m_j - M);
-// each wave forms sum_j e_j l_j and sum_j e_j acc_j[d] over its chunks in chunk
-// order, and wave 0 adds the waves' sums in wave order and divides.
-constexpr int kMergeWaves = 4;
-constexpr int kMergePer = kMergeMaxChunks / kMergeWaves;  // chunks per wave, at most
+// One workgroup per (query, head) folds the chunk partials, one wave per 32
+// chunks (nw = ceil(nchunks / 32) waves, at most 16), so every wave issues all
+// of its loads at once and the fold costs one round trip to memory at any k:
+// M = max m_j over all chunks, e_j = exp(m_j - M); wave w forms
+// sum_j e_j l_j and sum_j e_j acc_j[d] over its chunks in chunk order, and
+// wave 0 adds the waves' sums in wave order and divides.
+constexpr int kMergeChunksPerWave = 32;
+constexpr int kMergeMaxWaves = kMergeMaxChunks / kMergeChunksPerWave;
 
-__global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(
+__global__ __launch_bounds__(64 * kMergeMaxWaves) void attn_merge_kernel(
     const float *__restrict__ part, int heads, int dim, int nchunks, float *__restrict__ out) {
-  __shared__ float red[kMergeWaves][2 + 128];  // per wave: L, unused, acc[dim]
-  __shared__ float ew[kMergeMaxChunks];        // e_j of every chunk
-  __shared__ float wmax[kMergeWaves];
+  __shared__ float red[kMergeMaxWaves][2 + 128];  // per wave: L, unused, acc[dim]
+  __shared__ float ew[kMergeMaxChunks];           // e_j of every chunk
+  __shared__ float wmax[kMergeMaxWaves];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = t >> 6;
+  const int nw = blockDim.x >> 6;
   const int h = blockIdx.x;
   const int i = blockIdx.y;
   const int stride = dim + 4;
   const float *src = part + (int64_t(i) * heads + h) * nchunks * stride;
   float *o = out + (int64_t(i) * heads + h) * dim;
-  const int per = (nchunks + kMergeWaves - 1) / kMergeWaves;
-  const int j0 = w * per;
-  const int j1 = min(nchunks, j0 + per);
+  const int j0 = w * kMergeChunksPerWave;
+  const int nj = min(kMergeChunksPerWave, nchunks - j0);  // >= 1: nw = ceil(nchunks / 32)
 
-  // Every load of this wave first: the chunk maxima and sums (lane u holds
-  // chunks j0 + u, j0 + u + 64) and the value sums of the first 32 chunks;
-  // nothing here depends on the global maximum.
+  // Every load of this wave first: lane u < nj holds chunk j0 + u's maximum
+  // and sum; a0/a1 hold the value sums of all its chunks (dims lane, lane + 64).
   const bool d0 = lane < dim, d1 = lane + 64 < dim;
-  float mj[kMergePer / 64], lj[kMergePer / 64];
-  float a0[32], a1[32];
-#pragma unroll
-  for (int v = 0; v < kMergePer / 64; ++v) {
-    const int j = j0 + lane + 64 * v;
-    mj[v] = -INFINITY;
-    lj[v] = 0.f;
-    if (j < j1) {
-      mj[v] = src[int64_t(j) * stride];
-      lj[v] = src[int64_t(j) * stride + 1];
-    }
+  float mj = -INFINITY, lj = 0.f;
+  if (lane < nj) {
+    mj = src[int64_t(j0 + lane) * stride];
+    lj = src[int64_t(j0 + lane) * stride + 1];
   }
+  float a0[kMergeChunksPerWave], a1[kMergeChunksPerWave];
 #pragma unroll
-  for (int u = 0; u < 32; ++u) {
+  for (int u = 0; u < kMergeChunksPerWave; ++u) {
     const float *pj = src + int64_t(j0 + u) * stride + 4;
-    a0[u] = (j0 + u < j1 && d0) ? pj[lane] : 0.f;
-    a1[u] = (j0 + u < j1 && d1) ? pj[lane + 64] : 0.f;
+    a0[u] = (u < nj && d0) ? pj[lane] : 0.f;
+    a1[u] = (u < nj && d1) ? pj[lane + 64] : 0.f;
   }
-  float m = -INFINITY;
-#pragma unroll
-  for (int v = 0; v < kMergePer / 64; ++v) m = fmaxf(m, mj[v]);
-  m = group_all<1>(m, [](float x, float y) { return fmaxf(x, y); });
+  const float m = group_all<1>(mj, [](float x, float y) { return fmaxf(x, y); });
   if (lane == 0) wmax[w] = m;
   __syncthreads();
   float M = wmax[0];
-#pragma unroll
-  for (int u = 1; u < kMergeWaves; ++u) M = fmaxf(M, wmax[u]);
+  for (int u = 1; u < nw; ++u) M = fmaxf(M, wmax[u]);
   if (M == -INFINITY) {  // no attended cell
     if (w == 0)
       for (int d = lane; d < dim; d += 64) o[d] = 0.f;
     return;  // uniform across the workgroup
   }
-  float L = 0.f;
-#pragma unroll
-  for (int v = 0; v < kMergePer / 64; ++v) {
-    const float e = mj[v] == -INFINITY ? 0.f : expf(mj[v] - M);  // empty chunks weigh 0
-    if (j0 + lane + 64 * v < j1) ew[j0 + lane + 64 * v] = e;
-    L = __builtin_fmaf(lj[v], e, L);
-  }
-  L = group_all<1>(L, [](float x, float y) { return x + y; });
+  const float e = mj == -INFINITY ? 0.f : expf(mj - M);  // empty chunks weigh 0
+  if (lane < nj) ew[j0 + lane] = e;
+  const float L = group_all<1>(lj * e, [](float x, float y) { return x + y; });
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's weights are in LDS
   __builtin_amdgcn_wave_barrier();
 
   // Value sums over this wave's chunks, in chunk order.
   float acc0 = 0.f, acc1 = 0.f;
-  for (int jb = j0; jb < j1; jb += 32) {
-    if (jb > j0) {
 #pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const float *pj = src + int64_t(jb + u) * stride + 4;
-        a0[u] = (jb + u < j1 && d0) ? pj[lane] : 0.f;
-        a1[u] = (jb + u < j1 && d1) ? pj[lane + 64] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 32; ++u) {
-      const float e = jb + u < j1 ? ew[jb + u] : 0.f;
-      acc0 = __builtin_fmaf(a0[u], e, acc0);
-      acc1 = __builtin_fmaf(a1[u], e, acc1);
-    }
+  for (int u = 0; u < kMergeChunksPerWave; ++u) {
+    const float eu = u < nj ? ew[j0 + u] : 0.f;
+    acc0 = __builtin_fmaf(a0[u], eu, acc0);
+    acc1 = __builtin_fmaf(a1[u], eu, acc1);
   }
   if (lane == 0) red[w][0] = L;
   if (d0) red[w][2 + lane] = acc0;
@@ -391,8 +368,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(
   __syncthreads();
   if (w == 0) {
     float Lt = red[0][0], s0 = d0 ? red[0][2 + lane] : 0.f, s1 = d1 ? red[0][66 + lane] : 0.f;
-#pragma unroll
-    for (int u = 1; u < kMergeWaves; ++u) {
+    for (int u = 1; u < nw; ++u) {
       Lt += red[u][0];
       if (d0) s0 += red[u][2 + lane];
       if (d1) s1 += red[u][66 + lane];
@@ -434,8 +410,8 @@ hipError_t chunk_partials(hipStream_t stream, int nq, int heads, int dim, int k,
 
 hipError_t launch_merge(const float *part, int nq, int heads, int dim, int nchunks, float *out,
                         hipStream_t stream) {
-  attn_merge_kernel<<<dim3(heads, nq), 64 * kMergeWaves, 0, stream>>>(part, heads, dim, nchunks,
-                                                                      out);
+  const int nw = (nchunks + kMergeChunksPerWave - 1) / kMergeChunksPerWave;
+  attn_merge_kernel<<<dim3(heads, nq), 64 * nw, 0, stream>>>(part, heads, dim, nchunks, out);
   return hipGetLastError();
 }
 
