@@ -82,6 +82,8 @@ def parse_args():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default=synth.HEADLINE, choices=list(synth.WORKLOADS))
+    p.add_argument("--k", type=int, default=None,
+                   help="blocks selected per query (default: the workload's k)")
     p.add_argument("--copies", type=int, default=6,
                    help="input copies rotated over the steps (defeats cache reuse)")
     p.add_argument("--scores-mode", default="auto", choices=["auto", "fp32", "bf16x3"],
@@ -235,6 +237,10 @@ def main():
         return
 
     w = synth.WORKLOADS[args.workload]
+    if args.k is not None:
+        import dataclasses
+        if args.k != w.k:  # a different workload: no published figure, no stored counters
+            w = dataclasses.replace(w, name=f"{w.name}-k{args.k}", k=args.k)
     bt = synth.make_batch(w)
     ncopy = max(1, args.copies)
     q_d = [torch.from_numpy(bt.q).to(dev) for _ in range(ncopy)]

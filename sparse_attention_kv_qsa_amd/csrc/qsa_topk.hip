@@ -458,10 +458,19 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
 //   the row runs the one-workgroup selection on the row instead; the result
 //   is the same.
 // ---------------------------------------------------------------------------
-constexpr int WIDE_NB = 16;      // rank workgroups per row (a power of two)
-constexpr int WIDE_CCAP = 4096;  // LDS candidate capacity
-constexpr int WIDE_UCAP = 8192;  // published words per row, at most
-constexpr int WIDE_RCAP = 1024;  // rich groups listed (more: the one-workgroup fallback)
+constexpr int WIDE_CCAP = 8192;   // LDS candidate capacity
+constexpr int WIDE_UCAP = 16384;  // published words per row, at most
+constexpr int WIDE_GCAP = WIDE_UCAP / 4;  // groups per row, at most (each publishes >= 4)
+constexpr int WIDE_RCAP = 1024;   // rich groups listed (more: the one-workgroup fallback)
+
+// Rank workgroups per row: the exact-rank step costs about C^2 / NB word
+// comparisons per workgroup for C ~ k candidates, so NB grows with k (16 at
+// k <= 512, 128 at k = 4096) and every workgroup's share stays the same.
+int wide_nb(int k) {
+  int nb = 16;
+  while (nb < 128 && nb * 32 < k) nb *= 2;
+  return nb;
+}
 
 
 // Wave maximum of a rank word held as (key, ~id) halves, using lane_xor
@@ -532,7 +541,7 @@ __global__ __launch_bounds__(256) void group_tops_kernel(const float *__restrict
 
 struct WideShared {
   uint32_t hist[4096];
-  uint64_t words[WIDE_UCAP];  // the row's published words
+  uint32_t lastk[WIDE_GCAP];  // each group's M-th published key
   uint64_t cand[WIDE_CCAP];
   uint32_t rich[WIDE_RCAP];
   uint32_t wsum[NWAVES];
@@ -558,7 +567,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wsum, 
   return before + incl - v;
 }
 
-template <int E>
+template <int E, int WPT>
 __global__ __launch_bounds__(NT) void wide_rank_kernel(const float *__restrict__ scores, int A,
                                                        int k, int *__restrict__ ids,
                                                        const uint64_t *__restrict__ tops,
@@ -577,9 +586,8 @@ __global__ __launch_bounds__(NT) void wide_rank_kernel(const float *__restrict__
 
   for (int i = t; i < 4096; i += NT) sh.hist[i] = 0;
   if (t == 0) sh.nvalid = 0;
-  // The published words, read once (their loads all in flight) and kept in
-  // LDS.
-  constexpr int WPT = WIDE_UCAP / NT;
+  // The published words, read once (their loads all in flight), WPT per
+  // thread (WPT * NT >= U).
   uint64_t wv[WPT];
 #pragma unroll
   for (int i = 0; i < WPT; ++i) {
@@ -589,14 +597,16 @@ __global__ __launch_bounds__(NT) void wide_rank_kernel(const float *__restrict__
   __syncthreads();
 
   // (a) the bound: histogram of the published keys' top 12 bits, then the
-  // bin where the count from the top reaches k.
+  // bin where the count from the top reaches k.  Each group's M-th key goes
+  // to LDS for (b).
+  const int lgM = __builtin_ctz(uint32_t(M));  // M is a power of two
   uint32_t nv = 0;
 #pragma unroll
   for (int i = 0; i < WPT; ++i) {
     const int e = t + i * NT;
     if (e >= U) break;
-    sh.words[e] = wv[i];
     const uint32_t key = uint32_t(wv[i] >> 32);
+    if ((e & (M - 1)) == M - 1) sh.lastk[e >> lgM] = key;
     if (key) {
       atomicAdd(&sh.hist[key >> 20], 1u);
       ++nv;
@@ -628,7 +638,6 @@ __global__ __launch_bounds__(NT) void wide_rank_kernel(const float *__restrict__
   // (b) candidates, in an order every workgroup of the row agrees on: the
   // published words >= B of complete groups (thread order, then slot
   // order), then the elements >= B of the rich groups.
-  const int lgM = __builtin_ctz(uint32_t(M));  // M is a power of two
   bool take[WPT], rich[WPT];
   uint32_t ntake = 0, nrich = 0;
 #pragma unroll
@@ -637,7 +646,7 @@ __global__ __launch_bounds__(NT) void wide_rank_kernel(const float *__restrict__
     take[i] = rich[i] = false;
     if (e < U) {
       const int g = e >> lgM;
-      const uint32_t last = uint32_t(sh.words[(g << lgM) + (M - 1)] >> 32);
+      const uint32_t last = sh.lastk[g];
       const bool complete = last < B;
       take[i] = complete && uint32_t(wv[i] >> 32) >= B;
       rich[i] = !complete && (e == (g << lgM));
@@ -739,6 +748,19 @@ __global__ __launch_bounds__(NT) void wide_rank_kernel(const float *__restrict__
     for (int r = m + t; r < k; r += NT) orow[r] = -1;
 }
 
+// The rank kernel with WPT = 8 words per thread when the row publishes at
+// most 8192 (decode at k <= ~2048), else 16.
+template <int E>
+hipError_t launch_rank(const float *scores, int nq, int A, int k, int *ids, const uint64_t *tops,
+                       int ngroups, int M, hipStream_t stream) {
+  const dim3 grid(wide_nb(k), nq);
+  if (ngroups * M <= 8 * NT)
+    wide_rank_kernel<E, 8><<<grid, NT, 0, stream>>>(scores, A, k, ids, tops, ngroups, M);
+  else
+    wide_rank_kernel<E, WIDE_UCAP / NT><<<grid, NT, 0, stream>>>(scores, A, k, ids, tops, ngroups, M);
+  return hipGetLastError();
+}
+
 template <int E>
 hipError_t launch_wide(const float *scores, int nq, int A, int k, int *ids, hipStream_t stream) {
   constexpr int GS = 64 * E;
@@ -749,8 +771,7 @@ hipError_t launch_wide(const float *scores, int nq, int A, int k, int *ids, hipS
   if (e != hipSuccess) return e;
   uint64_t *tops = static_cast<uint64_t *>(ws);
   group_tops_kernel<E><<<dim3((ngroups + 3) / 4, nq), 256, 0, stream>>>(scores, A, ngroups, M, tops);
-  wide_rank_kernel<E><<<dim3(WIDE_NB, nq), NT, 0, stream>>>(scores, A, k, ids, tops, ngroups, M);
-  return hipGetLastError();
+  return launch_rank<E>(scores, nq, A, k, ids, tops, ngroups, M, stream);
 }
 
 template <int PER>
@@ -774,8 +795,7 @@ int wide_words_per_group(int ngroups, int k) {
 hipError_t launch_wide_rank(const float *scores, int nq, int A, int k, int *ids,
                             const uint64_t *tops, int M, hipStream_t stream) {
   const int ngroups = (A + 63) / 64;
-  wide_rank_kernel<1><<<dim3(WIDE_NB, nq), NT, 0, stream>>>(scores, A, k, ids, tops, ngroups, M);
-  return hipGetLastError();
+  return launch_rank<1>(scores, nq, A, k, ids, tops, ngroups, M, stream);
 }
 
 hipError_t launch_block_topk(const float *scores, int nq, int A, int k, int *ids,

@@ -183,7 +183,7 @@ WIDTH_CASES = [
     (1, 1), (2, 1), (17, 5), (512, 64), (1023, 100), (1024, 1024), (1025, 1),
     (2048, 300), (2049, 2048), (4096, 4095), (4097, 512), (8193, 256), (16385, 700),
     (24577, 1000), (32770, 512), (33792, 33), (33793, 4096), (49153, 999), (65538, 1024),
-    (66560, 2), (66561, 300), (100003, 1024),
+    (66560, 2), (66561, 300), (100003, 1024), (32770, 4096), (32770, 2049),
 ]
 
 
@@ -291,6 +291,8 @@ SELECT_CASES = [  # nq, heads, dim, active, k  (nq <= 8 with K <= 4096/nq fuse; 
     (3, 2, 128, 777, 50), (8, 4, 128, 8193, 256), (1, 8, 256, 3000, 128), (1, 16, 256, 640, 64),
     (4, 4, 256, 2049, 300), (5, 2, 64, 65, 7), (1, 1, 4, 70, 5), (1, 4, 128, 63, 4096),
     (9, 4, 128, 3000, 256), (1, 4, 128, 131073, 64), (40, 4, 128, 2000, 100), (8, 8, 128, 300, 30),
+    # decode at large k: more published words than 8 per thread, up to 128 rank workgroups
+    (1, 4, 128, 32770, 4096), (4, 4, 128, 32770, 2048), (2, 4, 128, 33793, 3000),
 ]
 
 
