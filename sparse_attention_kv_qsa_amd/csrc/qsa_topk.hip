@@ -351,31 +351,47 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
   };
   __syncthreads();
 
-  // Candidate bound.  Every thread's maximum over its own slots is a distinct
-  // element of the row.  Each wave sorts its 64 thread maxima (descending,
-  // lane exchanges only) and takes the kw-th, kw = ceil(k / 16): at least kw
-  // of its maxima are >= it.  The smallest of the 16 wave values is then
-  // exceeded-or-equalled by at least 16 * kw >= k elements, so it is <= the
-  // k-th largest key and every winner lies at or above it.  Without enough
-  // groups (k > 1024) the bound is 1: every real key is a candidate.
+  // Candidate bound.  Every thread's two largest keys over its own slots are
+  // two distinct elements of the row (or sentinels).  Each wave finds the
+  // kw-th largest, kw = ceil(k / 16), of its 128 such values: at least kw
+  // elements of the wave are >= it.  The smallest of the 16 wave values is
+  // then exceeded-or-equalled by at least 16 * kw >= k elements, so it is <=
+  // the k-th largest key and every winner lies at or above it.  (With one
+  // value per thread the bound sat lower: about 3 % of an N(0,1) row passed
+  // it and one row in ten overflowed the direct sort; with two, about 2 %.)
+  // Without enough groups (k > 1024) the bound is 1: every real key is a
+  // candidate.
   uint32_t bound = 1u;
   if (k < A && k <= NT) {
-    uint32_t v = 0u;
+    uint32_t v1 = 0u, v2 = 0u;  // this thread's largest and second-largest keys
+    auto take = [&](uint32_t x) {
+      v2 = max(v2, min(v1, x));
+      v1 = max(v1, x);
+    };
     if constexpr (PER >= 0) {
 #pragma unroll
-      for (int j = 0; j < PER; ++j) v = max(v, rk.key[j]);
-      v = max(v, sh.extra[t]);
+      for (int j = 0; j < PER; ++j) take(rk.key[j]);
+      take(sh.extra[t]);
     } else {
-      for (int base = 0; base < A; base += NT) v = max(v, load_key(base + t));
+      for (int base = 0; base < A; base += NT) take(load_key(base + t));
     }
-    // Wave-local bitonic sort of the 64 maxima, descending (the id slot is unused).
+    // Wave-local bitonic sorts of both lists, descending (the id slot is
+    // unused); then the elementwise maximum of the first list and the second
+    // reversed holds the 64 largest of the 128 as a bitonic sequence, and one
+    // more merge stage puts them in descending order.
     auto greater = [](uint32_t ka, uint32_t, uint32_t kb, uint32_t) { return ka > kb; };
     uint32_t unused = 0u;
-    bitonic_lane_stage<2, 1>(v, unused, lane, greater);
-    bitonic_lane_stage<4, 2>(v, unused, lane, greater);
-    bitonic_lane_stage<8, 4>(v, unused, lane, greater);
-    bitonic_lane_stage<16, 8>(v, unused, lane, greater);
-    bitonic_lane_stage<32, 16>(v, unused, lane, greater);
+    auto sort64 = [&](uint32_t &v) {
+      bitonic_lane_stage<2, 1>(v, unused, lane, greater);
+      bitonic_lane_stage<4, 2>(v, unused, lane, greater);
+      bitonic_lane_stage<8, 4>(v, unused, lane, greater);
+      bitonic_lane_stage<16, 8>(v, unused, lane, greater);
+      bitonic_lane_stage<32, 16>(v, unused, lane, greater);
+      bitonic_lane_stage<64, 32>(v, unused, lane, greater);
+    };
+    sort64(v1);
+    sort64(v2);
+    uint32_t v = max(v1, uint32_t(__shfl(int(v2), 63 - lane, 64)));
     bitonic_lane_stage<64, 32>(v, unused, lane, greater);
     const int kw = (k + NWAVES - 1) / NWAVES;
     const uint32_t vw = __builtin_amdgcn_readlane(v, kw - 1);
