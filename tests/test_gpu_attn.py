@@ -223,3 +223,60 @@ def test_attention_i8_full_size_after_selection():
     _, ids = qsa_block_select(torch.from_numpy(bt.q).cuda(), torch.from_numpy(bt.kblk).cuda(), w.k,
                               w.active)
     check_attn_i8(bt.q, kq, ks, vq, vs, ids.cpu().numpy(), 4 * w.active, 1.0 / np.sqrt(w.dim))
+
+
+@pytest.mark.parametrize("nq,active,k", [(1, 5000, 256), (3, 20000, 1024), (20, 3000, 100)])
+def test_decode_layer_replays_from_a_graph(nq, active, k):
+    """Select then attention (both pools) captured into one HIP graph on a side
+    stream: every replay, with eager library calls and synchronisations
+    between replays, reproduces the eager outputs bitwise.  (nq = 20 takes
+    the one-workgroup-per-row top-k, the others the whole-GPU one.)"""
+    from sparse_attention_kv_qsa_amd import (qsa_block_select, qsa_sparse_decode_attention,
+                                             qsa_sparse_decode_attention_i8)
+    heads, dim = 4, 64
+    q, kb = synth.make_random(nq, heads, dim, active, capacity=active + 2, seed=active + nq)
+    rng = np.random.default_rng(nq)
+    cells = 4 * (active + 2)
+    kc = rng.standard_normal((cells, heads, dim)).astype(np.float32)
+    vc = rng.standard_normal((cells, heads, dim)).astype(np.float32)
+    kq, ks = synth.make_pool_i8(cells, 4 * active, heads, dim, seed=3)
+    vq, vs = synth.make_pool_i8(cells, 4 * active, heads, dim, seed=4)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    qd, kbd, kcd, vcd = t(q), t(kb), t(kc), t(vc)
+    pool = (t(kq), t(ks.view(np.int16)), t(vq), t(vs.view(np.int16)))
+    scores = torch.empty((nq, active), dtype=torch.float32, device="cuda")
+    ids = torch.empty((nq, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((nq, heads, dim), dtype=torch.float32, device="cuda")
+    out8 = torch.empty_like(out)
+
+    def layer():
+        qsa_block_select(qd, kbd, k, active, scores=scores, ids=ids)
+        qsa_sparse_decode_attention(qd, kcd, vcd, ids, 4 * active, out=out)
+        qsa_sparse_decode_attention_i8(qd, *pool, ids, 4 * active, out=out8)
+
+    layer()
+    torch.cuda.synchronize()
+    want = [x.clone() for x in (scores, ids, out, out8)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()  # the library's scratch for this stream is allocated here, not in the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        layer()
+    torch.cuda.synchronize()
+    other = t(synth.make_random(nq, heads, dim, active, capacity=active + 2, seed=99)[0])
+    for rep in range(3):
+        for x in (scores, ids, out, out8):
+            x.fill_(-3)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, x, y in zip(("scores", "ids", "out", "out8"), (scores, ids, out, out8), want):
+            assert torch.equal(x, y), f"replay {rep}: {name} differs from the eager result"
+        # eager work on the default stream between replays
+        qsa_block_select(other, kbd, k, active)
+        torch.cuda.synchronize()
+    # the eager outputs are still the expected ones after the replays
+    check_attn(q, kc, vc, want[1].cpu().numpy(), 4 * active, 1.0 / np.sqrt(dim))
