@@ -353,7 +353,8 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
 
   // Candidate bound.  Every thread's two largest keys over its own slots are
   // two distinct elements of the row (or sentinels).  Each wave finds the
-  // kw-th largest, kw = ceil(k / 16), of its 128 such values: at least kw
+  // kw-th largest, kw = ceil(k / 16), of its 128 such values (a bisection on
+  // the key bits with wave ballots, cheaper than sorting them): at least kw
   // elements of the wave are >= it.  The smallest of the 16 wave values is
   // then exceeded-or-equalled by at least 16 * kw >= k elements, so it is <=
   // the k-th largest key and every winner lies at or above it.  (With one
@@ -375,26 +376,16 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
     } else {
       for (int base = 0; base < A; base += NT) take(load_key(base + t));
     }
-    // Wave-local bitonic sorts of both lists, descending (the id slot is
-    // unused); then the elementwise maximum of the first list and the second
-    // reversed holds the 64 largest of the 128 as a bitonic sequence, and one
-    // more merge stage puts them in descending order.
-    auto greater = [](uint32_t ka, uint32_t, uint32_t kb, uint32_t) { return ka > kb; };
-    uint32_t unused = 0u;
-    auto sort64 = [&](uint32_t &v) {
-      bitonic_lane_stage<2, 1>(v, unused, lane, greater);
-      bitonic_lane_stage<4, 2>(v, unused, lane, greater);
-      bitonic_lane_stage<8, 4>(v, unused, lane, greater);
-      bitonic_lane_stage<16, 8>(v, unused, lane, greater);
-      bitonic_lane_stage<32, 16>(v, unused, lane, greater);
-      bitonic_lane_stage<64, 32>(v, unused, lane, greater);
-    };
-    sort64(v1);
-    sort64(v2);
-    uint32_t v = max(v1, uint32_t(__shfl(int(v2), 63 - lane, 64)));
-    bitonic_lane_stage<64, 32>(v, unused, lane, greater);
+    // The wave's kw-th largest of its 128 values, bit by bit from the top:
+    // the largest x with at least kw values >= x (counted with two ballots
+    // per bit; x stays wave-uniform).
     const int kw = (k + NWAVES - 1) / NWAVES;
-    const uint32_t vw = __builtin_amdgcn_readlane(v, kw - 1);
+    uint32_t vw = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = vw | (1u << bit);
+      const uint32_t n = uint32_t(__popcll(__ballot(v1 >= c))) + uint32_t(__popcll(__ballot(v2 >= c)));
+      if (n >= uint32_t(kw)) vw = c;
+    }
     if (lane == 0) sh.wmin[wave] = vw;
     __syncthreads();
     uint32_t b = 0xFFFFFFFFu;
