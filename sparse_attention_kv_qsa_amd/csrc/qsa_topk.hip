@@ -42,7 +42,7 @@ constexpr int MAXK = kTopkMaxK;
 constexpr int CAP = 8192;  // LDS candidate capacity
 
 struct TopkShared {
-  uint64_t wbuf[NT];           // rank words of the sort's cross-wave steps
+  uint64_t wbuf[2 * NT];       // rank words of the sort's cross-wave steps (two buffers)
   uint32_t hsub[NWAVES][256];  // per-wave digit histograms
   uint32_t wtot[4];            // scan carry of the four scanning waves
   uint32_t bcast[3];           // chosen digit, remaining k, count in the bin
@@ -181,7 +181,7 @@ __device__ __forceinline__ void compact(Visit &&visit, Pred &&pred, uint32_t *co
 
 // Rank-order sort of the n (key, id) pairs in LDS arrays skey/sid (which the
 // large-P path also uses as scratch), then the store of one row of ids: the
-// first m in rank order, then -1 up to k.  `wbuf` is NT words of LDS scratch.
+// first m in rank order, then -1 up to k.  `wbuf` is 2 NT words of LDS scratch.
 // Every thread of the workgroup must call it.
 __device__ void sort_and_store(uint32_t *skey, uint32_t *sid, int n, int m, int k,
                                int *__restrict__ orow, uint64_t *wbuf) {
@@ -194,12 +194,17 @@ __device__ void sort_and_store(uint32_t *skey, uint32_t *sid, int n, int m, int 
     // Waves past the P elements only keep the barriers.
     const bool busy = (t & ~63) < P;  // wave-uniform
     uint64_t w = t < n ? rank_word(skey[t], sid[t]) : 0ull;
+    // Cross-wave steps alternate between two buffers, so each needs one
+    // barrier: a buffer is rewritten two steps after it was read, and every
+    // thread has passed the step in between.
+    int phase = 0;
     auto lds_step = [&](int size, int stride) {
-      __syncthreads();
-      if (busy) wbuf[t] = w;
+      uint64_t *buf = wbuf + (phase & 1) * NT;
+      ++phase;
+      if (busy) buf[t] = w;
       __syncthreads();
       if (busy) {
-        const uint64_t p = wbuf[t ^ stride];
+        const uint64_t p = buf[t ^ stride];
         const bool keep_larger = ((t & stride) == 0) == ((t & size) == 0);
         w = ((p > w) == keep_larger) ? p : w;
       }
