@@ -49,8 +49,13 @@ struct TopkShared {
   uint32_t ncand;              // candidates gathered
   uint32_t nwin;               // winners gathered
   uint32_t wmin[NWAVES];       // per-wave candidate bound
-  uint32_t ckey[CAP];          // candidates: keys ...
-  uint32_t cid[CAP];           // ... and block ids
+  union {
+    struct {
+      uint32_t ckey[CAP];      // candidates: keys ...
+      uint32_t cid[CAP];       // ... and block ids
+    } c;
+    uint64_t xbuf[CAP];        // the large sort's two exchange buffers, once the candidates are used
+  } cu;
   uint32_t bkey[MAXK];         // winners: keys ...
   uint32_t bid[MAXK];          // ... and ids, sorted into rank order
   uint32_t extra[NT];          // each thread's last key slot (kept in LDS, not VGPRs)
@@ -179,12 +184,105 @@ __device__ __forceinline__ void compact(Visit &&visit, Pred &&pred, uint32_t *co
   });
 }
 
-// Rank-order sort of the n (key, id) pairs in LDS arrays skey/sid (which the
-// large-P path also uses as scratch), then the store of one row of ids: the
-// first m in rank order, then -1 up to k.  `wbuf` is 2 NT words of LDS scratch.
-// Every thread of the workgroup must call it.
-__device__ void sort_and_store(uint32_t *skey, uint32_t *sid, int n, int m, int k,
-                               int *__restrict__ orow, uint64_t *wbuf) {
+// Bitonic sort of P = W NT rank words (descending), W words per thread: word r
+// of thread t is element i = t + NT r.  Strides of NT and more pair words of
+// one thread, strides 64 .. NT/2 go through LDS (two buffers alternating, one
+// barrier per step), smaller ones are lane exchanges.  The compare-exchange
+// rule is the one of the other sorts.
+template <int W>
+struct WideSort {
+  uint64_t w[W];
+  uint64_t *xbuf;  // 2 W NT words
+  int t;
+  int phase = 0;
+
+  template <int SIZE, int STRIDE>
+  __device__ __forceinline__ void step() {
+    if constexpr (STRIDE >= NT) {
+      constexpr int S = STRIDE / NT;  // the partner word of the same thread
+#pragma unroll
+      for (int r = 0; r < W; ++r) {
+        if constexpr (true) {
+          if ((r & S) == 0) {
+            const bool desc = ((t + NT * r) & SIZE) == 0;  // the lower element keeps the larger
+            const uint64_t a = w[r], b = w[r + S];
+            const uint64_t big = a > b ? a : b, small = a > b ? b : a;
+            w[r] = desc ? big : small;
+            w[r + S] = desc ? small : big;
+          }
+        }
+      }
+    } else {
+      uint64_t *buf = xbuf + (phase & 1) * (W * NT);
+      ++phase;
+#pragma unroll
+      for (int r = 0; r < W; ++r) buf[t + NT * r] = w[r];
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < W; ++r) {
+        const int i = t + NT * r;
+        const uint64_t p = buf[i ^ STRIDE];
+        const bool keep_larger = ((i & STRIDE) == 0) == ((i & SIZE) == 0);
+        w[r] = ((p > w[r]) == keep_larger) ? p : w[r];
+      }
+    }
+  }
+
+  // Stage SIZE: strides SIZE/2 .. 64 here, then 32 .. 1 inside each wave.
+  template <int SIZE, int STRIDE = SIZE / 2>
+  __device__ __forceinline__ void stage() {
+    if constexpr (STRIDE >= 64) {
+      step<SIZE, STRIDE>();
+      stage<SIZE, STRIDE / 2>();
+    } else {
+#pragma unroll
+      for (int r = 0; r < W; ++r) bitonic_word_stage<SIZE, (SIZE < 64 ? SIZE / 2 : 32)>(w[r], t + NT * r);
+    }
+  }
+};
+
+// The n (NT < n <= W NT) pairs of skey/sid in rank order: the first m ids to
+// orow, then -1 up to k.  `xbuf` holds 2 W NT words and does not overlap
+// skey/sid.
+template <int W>
+__device__ __forceinline__ void sort_wide(const uint32_t *skey, const uint32_t *sid, int n, int m, int k,
+                          int *__restrict__ orow, uint64_t *xbuf) {
+  WideSort<W> ws;
+  ws.xbuf = xbuf;
+  ws.t = threadIdx.x;
+  const int t = ws.t;
+#pragma unroll
+  for (int r = 0; r < W; ++r) {
+    const int i = t + NT * r;
+    ws.w[r] = i < n ? rank_word(skey[i], sid[i]) : 0ull;  // padding: word 0, after every element
+  }
+  ws.template stage<2>();
+  ws.template stage<4>();
+  ws.template stage<8>();
+  ws.template stage<16>();
+  ws.template stage<32>();
+  ws.template stage<64>();
+  ws.template stage<128>();
+  ws.template stage<256>();
+  ws.template stage<512>();
+  ws.template stage<1024>();
+  ws.template stage<2048>();
+  if constexpr (W >= 4) ws.template stage<4096>();
+#pragma unroll
+  for (int r = 0; r < W; ++r) {
+    const int i = t + NT * r;
+    if (i < m) orow[i] = int(~uint32_t(ws.w[r]));
+  }
+  for (int r = m + t; r < k; r += NT) orow[r] = -1;
+}
+
+// Rank-order sort of the n (key, id) pairs in LDS arrays skey/sid, then the
+// store of one row of ids: the first m in rank order, then -1 up to k.
+// `wbuf` is 2 NT words of LDS scratch; `xbuf`, 2 MAXK words, is used only
+// for n > NT and must not overlap skey/sid.  Every thread of the workgroup
+// must call it.
+__device__ __forceinline__ void sort_and_store(uint32_t *skey, uint32_t *sid, int n, int m, int k,
+                               int *__restrict__ orow, uint64_t *wbuf, uint64_t *xbuf) {
   const int t = threadIdx.x;
   int P = 1;
   while (P < n) P <<= 1;
@@ -245,33 +343,9 @@ __device__ void sort_and_store(uint32_t *skey, uint32_t *sid, int n, int m, int 
     for (int r = m + t; r < k; r += NT) orow[r] = -1;
     return;
   }
-  // P in (NT, MAXK]: bitonic network over LDS.
-  __syncthreads();
-  for (int i = n + t; i < P; i += NT) {
-    skey[i] = 0u;
-    sid[i] = 0xFFFFFFFFu;
-  }
-  __syncthreads();
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int p = t; p < (P >> 1); p += NT) {
-        const int i = ((p & ~(stride - 1)) << 1) | (p & (stride - 1));
-        const int j = i + stride;
-        const uint32_t ki = skey[i], kj = skey[j];
-        const uint32_t ii = sid[i], ij = sid[j];
-        const bool j_first = kj > ki || (kj == ki && ij < ii);
-        const bool forward = (i & size) == 0;
-        if (j_first == forward) {
-          skey[i] = kj;
-          skey[j] = ki;
-          sid[i] = ij;
-          sid[j] = ii;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int r = t; r < k; r += NT) orow[r] = r < m ? int(sid[r]) : -1;
+  // P in (NT, MAXK]: W = P / NT words per thread.
+  if (P == 2 * NT) sort_wide<2>(skey, sid, n, m, k, orow, xbuf);
+  else sort_wide<4>(skey, sid, n, m, k, orow, xbuf);
 }
 
 template <int PER>
@@ -356,39 +430,57 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
   };
   __syncthreads();
 
-  // Candidate bound.  Every thread's two largest keys over its own slots are
-  // two distinct elements of the row (or sentinels).  Each wave finds the
-  // kw-th largest, kw = ceil(k / 16), of its 128 such values (a bisection on
-  // the key bits with wave ballots, cheaper than sorting them): at least kw
-  // elements of the wave are >= it.  The smallest of the 16 wave values is
+  // Candidate bound.  Every thread's two (k > NT: four) largest keys over its
+  // own slots are distinct elements of the row (or sentinels).  Each wave
+  // finds the kw-th largest, kw = ceil(k / 16), of its 128 (256) such values
+  // (a bisection on the key bits with wave ballots, cheaper than sorting
+  // them): at least kw elements of the wave are >= it.  The smallest of the 16 wave values is
   // then exceeded-or-equalled by at least 16 * kw >= k elements, so it is <=
   // the k-th largest key and every winner lies at or above it.  (With one
   // value per thread the bound sat lower: about 3 % of an N(0,1) row passed
   // it and one row in ten overflowed the direct sort; with two, about 2 %.)
-  // Without enough groups (k > 1024) the bound is 1: every real key is a
-  // candidate.
+  // Beyond k = 4 NT the bound is 1: every real key is a candidate.
   uint32_t bound = 1u;
-  if (k < A && k <= NT) {
-    uint32_t v1 = 0u, v2 = 0u;  // this thread's largest and second-largest keys
-    auto take = [&](uint32_t x) {
+  if (k < A && k <= 4 * NT) {
+    // Up to k = NT each thread keeps its two largest keys, beyond that its
+    // four (kw <= 64 or 256 values of the wave are then enough).
+    const bool four = k > NT;  // workgroup-uniform
+    uint32_t v0 = 0u, v1 = 0u, v2 = 0u, v3 = 0u;  // this thread's largest keys, descending
+    auto take2 = [&](uint32_t x) {
+      v1 = max(v1, min(v0, x));
+      v0 = max(v0, x);
+    };
+    auto take4 = [&](uint32_t x) {
+      v3 = max(v3, min(v2, x));
       v2 = max(v2, min(v1, x));
-      v1 = max(v1, x);
+      take2(x);
     };
     if constexpr (PER >= 0) {
+      if (four) {
 #pragma unroll
-      for (int j = 0; j < PER; ++j) take(rk.key[j]);
-      take(sh.extra[t]);
+        for (int j = 0; j < PER; ++j) take4(rk.key[j]);
+        take4(sh.extra[t]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) take2(rk.key[j]);
+        take2(sh.extra[t]);
+      }
     } else {
-      for (int base = 0; base < A; base += NT) take(load_key(base + t));
+      for (int base = 0; base < A; base += NT) {
+        const uint32_t x = load_key(base + t);
+        if (four) take4(x);
+        else take2(x);
+      }
     }
-    // The wave's kw-th largest of its 128 values, bit by bit from the top:
-    // the largest x with at least kw values >= x (counted with two ballots
-    // per bit; x stays wave-uniform).
+    // The wave's kw-th largest of its 128 (or 256) values, bit by bit from
+    // the top: the largest x with at least kw values >= x (counted with wave
+    // ballots; x stays wave-uniform).
     const int kw = (k + NWAVES - 1) / NWAVES;
     uint32_t vw = 0u;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t c = vw | (1u << bit);
-      const uint32_t n = uint32_t(__popcll(__ballot(v1 >= c))) + uint32_t(__popcll(__ballot(v2 >= c)));
+      uint32_t n = uint32_t(__popcll(__ballot(v0 >= c))) + uint32_t(__popcll(__ballot(v1 >= c)));
+      if (four) n += uint32_t(__popcll(__ballot(v2 >= c))) + uint32_t(__popcll(__ballot(v3 >= c)));
       if (n >= uint32_t(kw)) vw = c;
     }
     if (lane == 0) sh.wmin[wave] = vw;
@@ -399,15 +491,15 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
     bound = max(b, 1u);
   }
 
-  compact(visit_row, [&](uint32_t, uint32_t key) { return key >= bound; }, &sh.ncand, sh.ckey,
-          sh.cid, CAP);
+  compact(visit_row, [&](uint32_t, uint32_t key) { return key >= bound; }, &sh.ncand, sh.cu.c.ckey,
+          sh.cu.c.cid, CAP);
   __syncthreads();
   const uint32_t C = sh.ncand;
 
   if (C <= uint32_t(NT)) {
     // Few candidates (the usual case): sort them all into rank order and
     // keep the first m -- every winner is a candidate.
-    sort_and_store(sh.ckey, sh.cid, int(C), m, k, orow, sh.wbuf);
+    sort_and_store(sh.cu.c.ckey, sh.cu.c.cid, int(C), m, k, orow, sh.wbuf, nullptr);
     return;
   }
   if (C <= uint32_t(CAP)) {
@@ -416,7 +508,7 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
     auto visit_cand = [&](auto &&f) {
       for (uint32_t i = t; i < padC; i += NT) {
         const bool ok = i < C;
-        f(ok ? sh.cid[i] : 0u, ok ? sh.ckey[i] : 0u);
+        f(ok ? sh.cu.c.cid[i] : 0u, ok ? sh.cu.c.ckey[i] : 0u);
       }
     };
     Threshold th;
@@ -430,7 +522,7 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
             &sh.nwin, sh.bkey, sh.bid, MAXK);
   }
   __syncthreads();
-  sort_and_store(sh.bkey, sh.bid, m, m, k, orow, sh.wbuf);
+  sort_and_store(sh.bkey, sh.bid, m, m, k, orow, sh.wbuf, sh.cu.xbuf);
 }
 
 template <int PER>
