@@ -10,10 +10,11 @@
 //   out[i][h] = sum_c w_c v[c][h] / sum_c w_c        (0 if no cell).
 //
 // Two launches:
-//   1. attn_chunk_kernel: one wave per (query, head, chunk of kChunkBlocks
-//      listed blocks = up to 32 cells).  A cell row of `dim` fp32 is spread
-//      over LPC lanes (a float4 each; LPC = dim/4 rounded up to a power of
-//      two, dim <= 128), so one load instruction covers 64/LPC cells.  The wave first
+//   1. attn_chunk_kernel: one wave per (query, head, chunk of CB listed
+//      blocks = up to 4 * CB cells; CB = 4, 8 or 16 from k, see chunk_blocks).
+//      A cell row of `dim` fp32 is spread over LPC lanes (a float4 each;
+//      LPC = dim/4 rounded up to a power of two, dim <= 128), so one load
+//      instruction covers 64/LPC cells.  The wave first
 //      issues every key and value load of its chunk, then forms the dot
 //      products (4 FMAs per lane and an LPC-lane butterfly: a fixed tree),
 //      the chunk maximum m, the weights exp(s - m), their sum l and the
@@ -49,8 +50,6 @@ namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kChunkBlocks = 8;                // listed blocks per chunk
-constexpr int kChunkCells = 4 * kChunkBlocks;  // cells per chunk
 
 // Sum over the LPC lanes of a cell (lane bits below log2 LPC), the same tree in
 // every lane.
@@ -77,9 +76,9 @@ __device__ __forceinline__ float group_all(float v, Op op) {
   return v;
 }
 
-constexpr int kMergeMaxChunks = 512;  // QSA_TOPK_MAX_K / kChunkBlocks
+constexpr int kMergeMaxChunks = 512;  // QSA_TOPK_MAX_K / 8: chunk_blocks keeps nchunks below
 
-template <int LPC>
+template <int LPC, int CB>
 __global__ __launch_bounds__(64) void attn_chunk_kernel(const float *__restrict__ q,
                                                         const float *__restrict__ kc,
                                                         const float *__restrict__ vc,
@@ -87,7 +86,7 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(const float *__restrict_
                                                         int dim, int k, int n_cells, float scale,
                                                         float *__restrict__ part, int nchunks) {
   constexpr int CPI = 64 / LPC;                                    // cells per load instruction
-  constexpr int ROUNDS = kChunkCells / CPI > 0 ? kChunkCells / CPI : 1;  // loads per chunk
+  constexpr int ROUNDS = 4 * CB / CPI > 0 ? 4 * CB / CPI : 1;  // loads per chunk
   const int lane = threadIdx.x;
   const int chunk = blockIdx.x;
   const int h = blockIdx.y;
@@ -96,10 +95,10 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(const float *__restrict_
   const int grp = lane / LPC;                   // cell group of this lane
   const bool live = 4 * sub < dim;              // lanes past the row hold zeros
 
-  // The chunk's listed blocks, one per lane (lanes 0 .. kChunkBlocks-1).
-  const int j0 = chunk * kChunkBlocks;
+  // The chunk's listed blocks, one per lane (lanes 0 .. CB-1).
+  const int j0 = chunk * CB;
   int my_id = -1;
-  if (lane < kChunkBlocks && j0 + lane < k) my_id = ids[int64_t(i) * k + j0 + lane];
+  if (lane < CB && j0 + lane < k) my_id = ids[int64_t(i) * k + j0 + lane];
 
   const int64_t row = int64_t(heads) * dim;     // floats per cell
   const int64_t col = int64_t(h) * dim + 4 * sub;
@@ -112,7 +111,7 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(const float *__restrict_
     const int slot = r * CPI + grp;
     const int b = __shfl(my_id, (slot >> 2) & 63, 64);  // -1 past the chunk's blocks
     const int64_t c = int64_t(b) * 4 + (slot & 3);
-    ok[r] = slot < kChunkCells && b >= 0 && c < n_cells;
+    ok[r] = slot < 4 * CB && b >= 0 && c < n_cells;
     cell[r] = c;
   }
   // Every load of the chunk in flight at once (keys, then values); masked
@@ -179,13 +178,13 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(const float *__restrict_
 // dim/16 rounded up to a power of two, dim <= 128), so one load instruction
 // covers 64/LPC cells; the scales are one 2-byte load per cell (all LPC lanes
 // of a cell read the same address).
-template <int LPC>
+template <int LPC, int CB>
 __global__ __launch_bounds__(64) void attn_chunk_i8_kernel(
     const float *__restrict__ q, const int8_t *__restrict__ kq, const uint16_t *__restrict__ ks,
     const int8_t *__restrict__ vq, const uint16_t *__restrict__ vs, const int *__restrict__ ids,
     int heads, int dim, int k, int n_cells, float scale, float *__restrict__ part, int nchunks) {
   constexpr int CPI = 64 / LPC;
-  constexpr int ROUNDS = kChunkCells / CPI > 0 ? kChunkCells / CPI : 1;
+  constexpr int ROUNDS = 4 * CB / CPI > 0 ? 4 * CB / CPI : 1;
   const int lane = threadIdx.x;
   const int chunk = blockIdx.x;
   const int h = blockIdx.y;
@@ -194,9 +193,9 @@ __global__ __launch_bounds__(64) void attn_chunk_i8_kernel(
   const int grp = lane / LPC;
   const bool live = 16 * sub < dim;
 
-  const int j0 = chunk * kChunkBlocks;
+  const int j0 = chunk * CB;
   int my_id = -1;
-  if (lane < kChunkBlocks && j0 + lane < k) my_id = ids[int64_t(i) * k + j0 + lane];
+  if (lane < CB && j0 + lane < k) my_id = ids[int64_t(i) * k + j0 + lane];
 
   const int64_t row = int64_t(heads) * dim;  // codes per cell
   const int64_t col = int64_t(h) * dim + 16 * sub;
@@ -208,7 +207,7 @@ __global__ __launch_bounds__(64) void attn_chunk_i8_kernel(
     const int slot = r * CPI + grp;
     const int b = __shfl(my_id, (slot >> 2) & 63, 64);
     const int64_t c = int64_t(b) * 4 + (slot & 3);
-    ok[r] = slot < kChunkCells && b >= 0 && c < n_cells;
+    ok[r] = slot < 4 * CB && b >= 0 && c < n_cells;
     cell[r] = c;
   }
   uint4 kv[ROUNDS], vv[ROUNDS];
@@ -378,29 +377,83 @@ __global__ __launch_bounds__(64 * kMergeMaxWaves) void attn_merge_kernel(
   }
 }
 
-template <int LPC>
+template <int LPC, int CB>
 hipError_t launch_chunks(const float *q, const float *kc, const float *vc, const int *ids, int nq,
                          int heads, int dim, int k, int n_cells, float scale, float *part,
                          int nchunks, hipStream_t stream) {
-  attn_chunk_kernel<LPC><<<dim3(nchunks, heads, nq), 64, 0, stream>>>(
-      q, kc, vc, ids, heads, dim, k, n_cells, scale, part, nchunks);
-  return hipGetLastError();
+  if constexpr (4 * CB / (64 / LPC) > 16) {
+    return hipErrorInvalidValue;  // more rows than registers: never chosen
+  } else {
+    attn_chunk_kernel<LPC, CB><<<dim3(nchunks, heads, nq), 64, 0, stream>>>(
+        q, kc, vc, ids, heads, dim, k, n_cells, scale, part, nchunks);
+    return hipGetLastError();
+  }
 }
 
-template <int LPC>
+template <int CB>
+hipError_t chunks_f32(int lpc, const float *q, const float *kc, const float *vc, const int *ids,
+                      int nq, int heads, int dim, int k, int n_cells, float scale, float *part,
+                      int nchunks, hipStream_t stream) {
+  switch (lpc) {
+    case 1: return launch_chunks<1, CB>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream);
+    case 2: return launch_chunks<2, CB>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream);
+    case 4: return launch_chunks<4, CB>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream);
+    case 8: return launch_chunks<8, CB>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream);
+    case 16: return launch_chunks<16, CB>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream);
+    default: return launch_chunks<32, CB>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream);
+  }
+}
+
+template <int LPC, int CB>
 hipError_t launch_chunks_i8(const float *q, const int8_t *kq, const uint16_t *ks,
                             const int8_t *vq, const uint16_t *vs, const int *ids, int nq,
                             int heads, int dim, int k, int n_cells, float scale, float *part,
                             int nchunks, hipStream_t stream) {
-  attn_chunk_i8_kernel<LPC><<<dim3(nchunks, heads, nq), 64, 0, stream>>>(
-      q, kq, ks, vq, vs, ids, heads, dim, k, n_cells, scale, part, nchunks);
-  return hipGetLastError();
+  if constexpr (4 * CB / (64 / LPC) > 16) {
+    return hipErrorInvalidValue;  // more rows than registers: never chosen
+  } else {
+    attn_chunk_i8_kernel<LPC, CB><<<dim3(nchunks, heads, nq), 64, 0, stream>>>(
+        q, kq, ks, vq, vs, ids, heads, dim, k, n_cells, scale, part, nchunks);
+    return hipGetLastError();
+  }
+}
+
+template <int CB>
+hipError_t chunks_i8(int lpc, const float *q, const int8_t *kq, const uint16_t *ks,
+                     const int8_t *vq, const uint16_t *vs, const int *ids, int nq, int heads,
+                     int dim, int k, int n_cells, float scale, float *part, int nchunks,
+                     hipStream_t stream) {
+  switch (lpc) {
+    case 1: return launch_chunks_i8<1, CB>(q, kq, ks, vq, vs, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream);
+    case 2: return launch_chunks_i8<2, CB>(q, kq, ks, vq, vs, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream);
+    case 4: return launch_chunks_i8<4, CB>(q, kq, ks, vq, vs, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream);
+    default: return launch_chunks_i8<8, CB>(q, kq, ks, vq, vs, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream);
+  }
+}
+
+// Listed blocks per chunk wave: the smallest of 4, 8 and 16 that leaves at
+// most 256 chunks per (query, head), among those whose rows fit 128 VGPRs of
+// loads in flight (4 * cb cells over 64 / lpc cells per load, at most 16
+// loads of keys and 16 of values); else the largest that fits.  Measured on
+// one query and four heads: 4 blocks per wave at k = 512 (512 waves instead
+// of 256: -0.9 us fp32, -0.5 us int8 per call), 8 at k = 2048 (the merge of
+// 512 chunks costs more than the extra waves gain), 16 for int8 at 4 queries
+// and k = 4096 (-3 us).  k <= 4096 keeps every choice within kMergeMaxChunks.
+int chunk_blocks(int k, int lpc) {
+  int cb = 4;
+  for (int c = 4; c <= 16; c *= 2) {
+    if (4 * c * lpc / 64 > 16) break;
+    cb = c;
+    if ((k + c - 1) / c <= 256) break;
+  }
+  return cb;
 }
 
 // Chunk partials of nq * heads * nchunks chunks from the stream's scratch.
-hipError_t chunk_partials(hipStream_t stream, int nq, int heads, int dim, int k, int *nchunks,
-                          float **part) {
-  *nchunks = k > 0 ? (k + kChunkBlocks - 1) / kChunkBlocks : 1;
+hipError_t chunk_partials(hipStream_t stream, int nq, int heads, int dim, int k, int cb,
+                          int *nchunks, float **part) {
+  *nchunks = k > 0 ? (k + cb - 1) / cb : 1;
+  if (*nchunks > kMergeMaxChunks) return hipErrorInvalidValue;  // never chosen
   void *ws = nullptr;
   hipError_t e =
       workspace(stream, size_t(nq) * heads * *nchunks * (dim + 4) * sizeof(float), &ws);
@@ -424,18 +477,16 @@ hipError_t launch_sparse_decode_attention(const float *q, const float *kc, const
                                           const int *ids, int nq, int heads, int dim, int k,
                                           int n_cells, float scale, float *out,
                                           hipStream_t stream) {
+  const int lpc = dim <= 4 ? 1 : dim <= 8 ? 2 : dim <= 16 ? 4 : dim <= 32 ? 8 : dim <= 64 ? 16 : 32;
+  const int cb = chunk_blocks(k, lpc);
   int nchunks = 0;
   float *part = nullptr;
-  hipError_t e = chunk_partials(stream, nq, heads, dim, k, &nchunks, &part);
+  hipError_t e = chunk_partials(stream, nq, heads, dim, k, cb, &nchunks, &part);
   if (e != hipSuccess) return e;
-  const int lpc = dim <= 4 ? 1 : dim <= 8 ? 2 : dim <= 16 ? 4 : dim <= 32 ? 8 : dim <= 64 ? 16 : 32;
-  switch (lpc) {
-    case 1: e = launch_chunks<1>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
-    case 2: e = launch_chunks<2>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
-    case 4: e = launch_chunks<4>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
-    case 8: e = launch_chunks<8>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
-    case 16: e = launch_chunks<16>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
-    default: e = launch_chunks<32>(q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
+  switch (cb) {
+    case 4: e = chunks_f32<4>(lpc, q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
+    case 16: e = chunks_f32<16>(lpc, q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
+    default: e = chunks_f32<8>(lpc, q, kc, vc, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
   }
   if (e != hipSuccess) return e;
   return launch_merge(part, nq, heads, dim, nchunks, out, stream);
@@ -446,16 +497,16 @@ hipError_t launch_sparse_decode_attention_i8(const float *q, const int8_t *kq,
                                              const uint16_t *vs, const int *ids, int nq,
                                              int heads, int dim, int k, int n_cells,
                                              float scale, float *out, hipStream_t stream) {
+  const int lpc = dim <= 16 ? 1 : dim <= 32 ? 2 : dim <= 64 ? 4 : 8;
+  const int cb = chunk_blocks(k, lpc);
   int nchunks = 0;
   float *part = nullptr;
-  hipError_t e = chunk_partials(stream, nq, heads, dim, k, &nchunks, &part);
+  hipError_t e = chunk_partials(stream, nq, heads, dim, k, cb, &nchunks, &part);
   if (e != hipSuccess) return e;
-  const int lpc = dim <= 16 ? 1 : dim <= 32 ? 2 : dim <= 64 ? 4 : 8;
-  switch (lpc) {
-    case 1: e = launch_chunks_i8<1>(q, kq, ks, vq, vs, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
-    case 2: e = launch_chunks_i8<2>(q, kq, ks, vq, vs, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
-    case 4: e = launch_chunks_i8<4>(q, kq, ks, vq, vs, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
-    default: e = launch_chunks_i8<8>(q, kq, ks, vq, vs, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
+  switch (cb) {
+    case 4: e = chunks_i8<4>(lpc, q, kq, ks, vq, vs, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
+    case 16: e = chunks_i8<16>(lpc, q, kq, ks, vq, vs, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
+    default: e = chunks_i8<8>(lpc, q, kq, ks, vq, vs, ids, nq, heads, dim, k, n_cells, scale, part, nchunks, stream); break;
   }
   if (e != hipSuccess) return e;
   return launch_merge(part, nq, heads, dim, nchunks, out, stream);

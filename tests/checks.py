@@ -24,9 +24,10 @@ import numpy as np
 # FMA chain and a fixed lane tree, <= 9 levels at dim 128); an error e in
 # every score moves the normalised weights by at most ~2e relatively, hence
 # the second term with ATTN_SCORE_TOL = 2 * 12 * 2^-24 (margin included).
-# The weighted sums (<= 32 terms per lane, a 1-level lane tree), the chunk
-# merge (sequential over <= 512 chunks) and exp add a few 2^-24 of max|v|,
-# bounded by ATTN_TOL = 4e-6 at the sizes tested.
+# The weighted sums (<= 16 terms per lane, then a lane tree of <= 6 levels),
+# the chunk merge (<= 32 chunks in sequence per wave, <= 16 wave sums in
+# sequence) and exp add a few 2^-24 of max|v| (a convex combination), bounded
+# by ATTN_TOL = 4e-6 at the sizes tested.
 ATTN_TOL = 4e-6
 ATTN_SCORE_TOL = 2 * 12 * 2.0 ** -24
 # The int8 pool, gated on its dequantised rows: a lane's score sums 16
