@@ -1,8 +1,9 @@
 // Device scratch owned by the library.
 //
 // Some launches need a few bytes to megabytes of device memory beyond the
-// caller's inputs and outputs (the bf16 planes of the queries, the per-group
-// candidate lists of the top-k).  They come from one buffer per (device,
+// caller's inputs and outputs (the published group words of the few-row
+// top-k and of the fused decode select, the chunk partials of the decode
+// attention).  They come from one buffer per (device,
 // stream): work enqueued on one stream runs in order, so consecutive calls on
 // a stream can reuse the same bytes, and calls on different streams never
 // share them.  A buffer only grows; a buffer that is outgrown is kept (not
