@@ -54,7 +54,7 @@ extern "C" {
 /* Status codes. */
 #define QSA_OK 0
 #define QSA_ERR_NULL 1   /* a required pointer is NULL                              */
-#define QSA_ERR_SHAPE 2  /* a size < 0, heads*dim not a multiple of 4 in [4, QSA_MAX_HEAD_DIM], or a bad attention dim */
+#define QSA_ERR_SHAPE 2  /* a size < 0, heads*dim not a multiple of 4 in [4, QSA_MAX_HEAD_DIM], active_blocks > QSA_MAX_ACTIVE_BLOCKS, or a bad attention dim */
 #define QSA_ERR_K 3      /* k < 0 or k > QSA_TOPK_MAX_K                             */
 #define QSA_ERR_ALIGN 4  /* q or kblk not 16-byte aligned, scores/ids not 4-byte aligned */
 #define QSA_ERR_LAUNCH 5 /* the HIP runtime rejected a launch (hipGetLastError)     */
@@ -65,6 +65,10 @@ extern "C" {
 #define QSA_MAX_HEAD_DIM 4096
 /* Largest k accepted by qsa_block_topk. */
 #define QSA_TOPK_MAX_K 4096
+/* Largest active_blocks of the scoring and top-k calls (2^28 blocks = 2^30
+ * cells): a row of scores then stays below the 2^32 bytes one hardware
+ * buffer descriptor can address. */
+#define QSA_MAX_ACTIVE_BLOCKS 268435456
 /* qsa_block_topk spreads each row over the whole GPU when nq is at most this
  * (decode); larger batches select one row per workgroup.  Either way the
  * result is the same. */

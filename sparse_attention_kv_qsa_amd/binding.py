@@ -22,6 +22,7 @@ QSA_ERR_MODE = 6
 QSA_ERR_NOMEM = 7
 QSA_MAX_HEAD_DIM = 4096
 TOPK_MAX_K = 4096
+MAX_ACTIVE_BLOCKS = 1 << 28
 TOPK_FEW_ROWS = 16
 QSA_SCORES_AUTO, QSA_SCORES_FP32, QSA_SCORES_BF16X3 = 0, 1, 2
 QSA_ATTN_MAX_DIM = 128

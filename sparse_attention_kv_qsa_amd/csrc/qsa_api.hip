@@ -29,6 +29,7 @@ int launch_status(hipError_t e) {
 extern "C" int qsa_block_scores_ex(const float *q, const float *kblk, int nq, int heads, int dim,
                                    int active_blocks, float *scores, int mode, void *stream) {
   if (nq < 0 || heads < 0 || dim < 0 || active_blocks < 0) return QSA_ERR_SHAPE;
+  if (active_blocks > QSA_MAX_ACTIVE_BLOCKS) return QSA_ERR_SHAPE;
   const int64_t K = int64_t(heads) * dim;
   if (K < 4 || K % 4 != 0 || K > QSA_MAX_HEAD_DIM) return QSA_ERR_SHAPE;
   if (mode != QSA_SCORES_AUTO && mode != QSA_SCORES_FP32 && mode != QSA_SCORES_BF16X3)
@@ -49,7 +50,7 @@ extern "C" int qsa_block_scores(const float *q, const float *kblk, int nq, int h
 
 extern "C" int qsa_block_topk(const float *scores, int nq, int active_blocks, int k, int *ids,
                               void *stream) {
-  if (nq < 0 || active_blocks < 0) return QSA_ERR_SHAPE;
+  if (nq < 0 || active_blocks < 0 || active_blocks > QSA_MAX_ACTIVE_BLOCKS) return QSA_ERR_SHAPE;
   if (k < 0 || k > QSA_TOPK_MAX_K) return QSA_ERR_K;
   if (nq == 0 || k == 0) return QSA_OK;
   if (!ids || (active_blocks > 0 && !scores)) return QSA_ERR_NULL;
@@ -62,6 +63,7 @@ extern "C" int qsa_block_topk(const float *scores, int nq, int active_blocks, in
 extern "C" int qsa_block_select(const float *q, const float *kblk, int nq, int heads, int dim,
                                 int active_blocks, int k, float *scores, int *ids, void *stream) {
   if (nq < 0 || heads < 0 || dim < 0 || active_blocks < 0) return QSA_ERR_SHAPE;
+  if (active_blocks > QSA_MAX_ACTIVE_BLOCKS) return QSA_ERR_SHAPE;
   const int64_t K = int64_t(heads) * dim;
   if (K < 4 || K % 4 != 0 || K > QSA_MAX_HEAD_DIM) return QSA_ERR_SHAPE;
   if (k < 0 || k > QSA_TOPK_MAX_K) return QSA_ERR_K;

@@ -46,6 +46,7 @@ def test_binding_covers_the_header():
         binding.QSA_OK, binding.QSA_ERR_NULL, binding.QSA_ERR_SHAPE, binding.QSA_ERR_K,
         binding.QSA_ERR_ALIGN, binding.QSA_ERR_LAUNCH)
     assert mac["QSA_TOPK_MAX_K"] == binding.TOPK_MAX_K
+    assert mac["QSA_MAX_ACTIVE_BLOCKS"] == binding.MAX_ACTIVE_BLOCKS
     assert mac["QSA_TOPK_FEW_ROWS"] == binding.TOPK_FEW_ROWS
     assert mac["QSA_ERR_MODE"] == binding.QSA_ERR_MODE
     assert mac["QSA_ERR_NOMEM"] == binding.QSA_ERR_NOMEM
@@ -88,6 +89,7 @@ P4 = 0x10004
     ((P16, P16, -1, 4, 128, 10, P16), binding.QSA_ERR_SHAPE),   # nq < 0
     ((P16, P16, 1, -4, 128, 10, P16), binding.QSA_ERR_SHAPE),   # heads < 0
     ((P16, P16, 1, 4, 128, -1, P16), binding.QSA_ERR_SHAPE),    # active < 0
+    ((P16, P16, 1, 4, 128, (1 << 28) + 1, P16), binding.QSA_ERR_SHAPE),  # active too large
     ((P16, P16, 1, 3, 3, 10, P16), binding.QSA_ERR_SHAPE),      # K = 9, not a multiple of 4
     ((P16, P16, 1, 2, 4097, 10, P16), binding.QSA_ERR_SHAPE),   # K > 4096
     ((P16, P16, 1, 0, 128, 10, P16), binding.QSA_ERR_SHAPE),    # K = 0
@@ -113,6 +115,7 @@ def test_block_scores_ex_mode_check(lib, mode, status):
 @pytest.mark.parametrize("args,status", [
     ((P16, -1, 10, 4, P16), binding.QSA_ERR_SHAPE),
     ((P16, 1, -1, 4, P16), binding.QSA_ERR_SHAPE),
+    ((P16, 1, (1 << 28) + 1, 4, P16), binding.QSA_ERR_SHAPE),   # active > QSA_MAX_ACTIVE_BLOCKS
     ((P16, 1, 10, -1, P16), binding.QSA_ERR_K),
     ((P16, 1, 10, 4097, P16), binding.QSA_ERR_K),
     ((None, 1, 10, 4, P16), binding.QSA_ERR_NULL),
@@ -131,6 +134,7 @@ def test_block_topk_argument_checks(lib, args, status):
     ((P16, P16, -1, 4, 128, 10, 4, P16, P16), binding.QSA_ERR_SHAPE),
     ((P16, P16, 1, 3, 3, 10, 4, P16, P16), binding.QSA_ERR_SHAPE),
     ((P16, P16, 1, 4, 128, -1, 4, P16, P16), binding.QSA_ERR_SHAPE),
+    ((P16, P16, 1, 4, 128, (1 << 28) + 1, 4, P16, P16), binding.QSA_ERR_SHAPE),
     ((P16, P16, 1, 4, 128, 10, -1, P16, P16), binding.QSA_ERR_K),
     ((P16, P16, 1, 4, 128, 10, 4097, P16, P16), binding.QSA_ERR_K),
     ((None, P16, 1, 4, 128, 10, 4, P16, P16), binding.QSA_ERR_NULL),
