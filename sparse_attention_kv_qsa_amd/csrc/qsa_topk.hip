@@ -115,6 +115,22 @@ struct Threshold {
   }
 };
 
+// Count `bin` into the wave's sub-histogram for the lanes where `take` holds.
+// The lanes sharing the first such lane's bin add their count with one
+// atomic: radix digits are often shared by most of the wave (the leading
+// digit of keys of one magnitude, mass ties), and same-address LDS atomics
+// serialise.  Every lane of the wave must call it.
+__device__ __forceinline__ void hist_add(uint32_t *hsub, bool take, uint32_t bin) {
+  const uint64_t act = __ballot(take);
+  if (act == 0) return;  // wave-uniform
+  const int first = __builtin_ctzll(act);
+  const uint32_t lead = __builtin_amdgcn_readlane(bin, first);
+  const bool same = take && bin == lead;
+  const uint64_t nsame = __popcll(__ballot(same));
+  if ((threadIdx.x & 63) == first) atomicAdd(&hsub[lead], uint32_t(nsame));
+  else if (take && !same) atomicAdd(&hsub[bin], 1u);
+}
+
 // Radix select of the k largest (key, id) pairs among those `visit` yields
 // (key 0 = sentinel; n_sentinel of them among the visited).  k must be less
 // than the number of real keys.  ids are block ids < A.
@@ -127,7 +143,7 @@ __device__ __forceinline__ Threshold radix_select(TopkShared &sh, Visit &&visit,
   for (int shift = 24; shift >= 0; shift -= 8) {
     const uint32_t mask = th.mask, pref = th.pref;
     visit([&](uint32_t, uint32_t key) {
-      if ((key & mask) == pref) atomicAdd(&sh.hsub[wave][(key >> shift) & 255u], 1u);
+      hist_add(sh.hsub[wave], (key & mask) == pref, (key >> shift) & 255u);
     });
     __syncthreads();
     uint32_t d, cnt;
@@ -144,7 +160,7 @@ __device__ __forceinline__ Threshold radix_select(TopkShared &sh, Visit &&visit,
     const uint32_t T = th.pref, idmask = th.idmask, idpref = th.idpref, idtop = th.idtop;
     visit([&](uint32_t id, uint32_t key) {
       const uint32_t rid = idtop - id;
-      if (key == T && (rid & idmask) == idpref) atomicAdd(&sh.hsub[wave][(rid >> shift) & 255u], 1u);
+      hist_add(sh.hsub[wave], key == T && (rid & idmask) == idpref, (rid >> shift) & 255u);
     });
     __syncthreads();
     uint32_t d, cnt;
