@@ -83,6 +83,8 @@ SHAPES = [  # nq, heads, dim, n_cells, k
     (2, 2, 96, 300, 17), (8, 4, 128, 600, 129), (1, 2, 128, 5, 1), (3, 4, 64, 257, 33),
     # chunks of 8 blocks (k in 1025..2048, or above at dim 128) and of 16 (dim 64, k > 2048)
     (1, 4, 128, 20000, 2000), (1, 4, 128, 17000, 3000), (2, 2, 64, 17000, 4096),
+    # the chunk-size boundaries: 256 chunks of 4 blocks, 129 of 8
+    (1, 4, 128, 9000, 1024), (1, 4, 128, 9000, 1025),
 ]
 
 
