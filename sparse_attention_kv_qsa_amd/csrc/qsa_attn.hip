@@ -19,8 +19,8 @@
 //      products (4 FMAs per lane and an LPC-lane butterfly: a fixed tree),
 //      the chunk maximum m, the weights exp(s - m), their sum l and the
 //      weighted value sum acc, and writes (m, l, acc[dim]).
-//   2. attn_merge_kernel: one workgroup per (query, head) folds the chunk
-//      partials: M = max m_j, L = sum l_j e^(m_j - M),
+//   2. attn_merge_kernel: one workgroup per (query, head, 64 dims) folds
+//      the chunk partials: M = max m_j, L = sum l_j e^(m_j - M),
 //      out = sum acc_j e^(m_j - M) / L, in a fixed order (each wave sums 32
 //      consecutive chunks, then the waves' sums are added in order).
 //      A fused variant (the last chunk wave of a (query, head) merging, found
@@ -296,19 +296,22 @@ __global__ __launch_bounds__(64) void attn_chunk_i8_kernel(
   }
 }
 
-// One workgroup per (query, head) folds the chunk partials, one wave per 32
-// chunks (nw = ceil(nchunks / 32) waves, at most 16), so every wave issues all
-// of its loads at once and the fold costs one round trip to memory at any k:
-// M = max m_j over all chunks, e_j = exp(m_j - M); wave w forms
-// sum_j e_j l_j and sum_j e_j acc_j[d] over its chunks in chunk order, and
-// wave 0 adds the waves' sums in wave order and divides.
+// One workgroup per (query, head, 64 dims of the row) folds the chunk
+// partials, one wave per 32 chunks (nw = ceil(nchunks / 32) waves, at most
+// 16), so every wave issues all of its loads at once and the fold costs one
+// round trip to memory at any k; a row of 128 dims is split over two
+// workgroups, which halves the bytes each CU loads.  M = max m_j over all
+// chunks, e_j = exp(m_j - M); wave w forms sum_j e_j l_j and sum_j e_j
+// acc_j[d] over its chunks in chunk order, and wave 0 adds the waves' sums in
+// wave order and divides.  (Both workgroups of a row form M, e_j and the l
+// sums identically.)
 constexpr int kMergeChunksPerWave = 32;
 constexpr int kMergeMaxWaves = kMergeMaxChunks / kMergeChunksPerWave;
 
 __global__ __launch_bounds__(64 * kMergeMaxWaves) void attn_merge_kernel(
     const float *__restrict__ part, int heads, int dim, int nchunks, float *__restrict__ out) {
-  __shared__ float red[kMergeMaxWaves][2 + 128];  // per wave: L, unused, acc[dim]
-  __shared__ float ew[kMergeMaxChunks];           // e_j of every chunk
+  __shared__ float red[kMergeMaxWaves][2 + 64];  // per wave: L, unused, acc[64 dims]
+  __shared__ float ew[kMergeMaxChunks];          // e_j of every chunk
   __shared__ float wmax[kMergeMaxWaves];
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -316,6 +319,7 @@ __global__ __launch_bounds__(64 * kMergeMaxWaves) void attn_merge_kernel(
   const int nw = blockDim.x >> 6;
   const int h = blockIdx.x;
   const int i = blockIdx.y;
+  const int d = 64 * int(blockIdx.z) + lane;  // this lane's dim
   const int stride = dim + 4;
   const float *src = part + (int64_t(i) * heads + h) * nchunks * stride;
   float *o = out + (int64_t(i) * heads + h) * dim;
@@ -323,28 +327,24 @@ __global__ __launch_bounds__(64 * kMergeMaxWaves) void attn_merge_kernel(
   const int nj = min(kMergeChunksPerWave, nchunks - j0);  // >= 1: nw = ceil(nchunks / 32)
 
   // Every load of this wave first: lane u < nj holds chunk j0 + u's maximum
-  // and sum; a0/a1 hold the value sums of all its chunks (dims lane, lane + 64).
-  const bool d0 = lane < dim, d1 = lane + 64 < dim;
+  // and sum; a0 holds dim d of the value sums of all its chunks.
+  const bool live = d < dim;
   float mj = -INFINITY, lj = 0.f;
   if (lane < nj) {
     mj = src[int64_t(j0 + lane) * stride];
     lj = src[int64_t(j0 + lane) * stride + 1];
   }
-  float a0[kMergeChunksPerWave], a1[kMergeChunksPerWave];
+  float a0[kMergeChunksPerWave];
 #pragma unroll
-  for (int u = 0; u < kMergeChunksPerWave; ++u) {
-    const float *pj = src + int64_t(j0 + u) * stride + 4;
-    a0[u] = (u < nj && d0) ? pj[lane] : 0.f;
-    a1[u] = (u < nj && d1) ? pj[lane + 64] : 0.f;
-  }
+  for (int u = 0; u < kMergeChunksPerWave; ++u)
+    a0[u] = (u < nj && live) ? src[int64_t(j0 + u) * stride + 4 + d] : 0.f;
   const float m = group_all<1>(mj, [](float x, float y) { return fmaxf(x, y); });
   if (lane == 0) wmax[w] = m;
   __syncthreads();
   float M = wmax[0];
   for (int u = 1; u < nw; ++u) M = fmaxf(M, wmax[u]);
   if (M == -INFINITY) {  // no attended cell
-    if (w == 0)
-      for (int d = lane; d < dim; d += 64) o[d] = 0.f;
+    if (w == 0 && live) o[d] = 0.f;
     return;  // uniform across the workgroup
   }
   const float e = mj == -INFINITY ? 0.f : expf(mj - M);  // empty chunks weigh 0
@@ -354,26 +354,22 @@ __global__ __launch_bounds__(64 * kMergeMaxWaves) void attn_merge_kernel(
   __builtin_amdgcn_wave_barrier();
 
   // Value sums over this wave's chunks, in chunk order.
-  float acc0 = 0.f, acc1 = 0.f;
+  float acc0 = 0.f;
 #pragma unroll
   for (int u = 0; u < kMergeChunksPerWave; ++u) {
     const float eu = u < nj ? ew[j0 + u] : 0.f;
     acc0 = __builtin_fmaf(a0[u], eu, acc0);
-    acc1 = __builtin_fmaf(a1[u], eu, acc1);
   }
   if (lane == 0) red[w][0] = L;
-  if (d0) red[w][2 + lane] = acc0;
-  if (d1) red[w][2 + 64 + lane] = acc1;
+  red[w][2 + lane] = acc0;
   __syncthreads();
   if (w == 0) {
-    float Lt = red[0][0], s0 = d0 ? red[0][2 + lane] : 0.f, s1 = d1 ? red[0][66 + lane] : 0.f;
+    float Lt = red[0][0], s0 = red[0][2 + lane];
     for (int u = 1; u < nw; ++u) {
       Lt += red[u][0];
-      if (d0) s0 += red[u][2 + lane];
-      if (d1) s1 += red[u][66 + lane];
+      s0 += red[u][2 + lane];
     }
-    if (d0) o[lane] = s0 / Lt;
-    if (d1) o[lane + 64] = s1 / Lt;
+    if (live) o[d] = s0 / Lt;
   }
 }
 
@@ -464,7 +460,8 @@ hipError_t chunk_partials(hipStream_t stream, int nq, int heads, int dim, int k,
 hipError_t launch_merge(const float *part, int nq, int heads, int dim, int nchunks, float *out,
                         hipStream_t stream) {
   const int nw = (nchunks + kMergeChunksPerWave - 1) / kMergeChunksPerWave;
-  attn_merge_kernel<<<dim3(heads, nq), 64 * nw, 0, stream>>>(part, heads, dim, nchunks, out);
+  attn_merge_kernel<<<dim3(heads, nq, (dim + 63) / 64), 64 * nw, 0, stream>>>(part, heads, dim,
+                                                                             nchunks, out);
   return hipGetLastError();
 }
 
