@@ -11,7 +11,7 @@
 //
 // Two launches:
 //   1. attn_chunk_kernel: one wave per (query, head, chunk of CB listed
-//      blocks = up to 4 * CB cells; CB = 4, 8 or 16 from k, see chunk_blocks).
+//      blocks = up to 4 * CB cells; CB = 4, 8 or 16, see chunk_blocks).
 //      A cell row of `dim` fp32 is spread over LPC lanes (a float4 each;
 //      LPC = dim/4 rounded up to a power of two, dim <= 128), so one load
 //      instruction covers 64/LPC cells.  The wave first
@@ -427,22 +427,21 @@ hipError_t chunks_i8(int lpc, const float *q, const int8_t *kq, const uint16_t *
   }
 }
 
-// Listed blocks per chunk wave: the smallest of 4, 8 and 16 that leaves at
-// most 256 chunks per (query, head), among those whose rows fit 128 VGPRs of
-// loads in flight (4 * cb cells over 64 / lpc cells per load, at most 16
-// loads of keys and 16 of values); else the largest that fits.  Measured on
-// one query and four heads: 4 blocks per wave at k = 512 (512 waves instead
-// of 256: -0.9 us fp32, -0.5 us int8 per call), 8 at k = 2048 (the merge of
-// 512 chunks costs more than the extra waves gain), 16 for int8 at 4 queries
-// and k = 4096 (-3 us).  k <= 4096 keeps every choice within kMergeMaxChunks.
-int chunk_blocks(int k, int lpc) {
-  int cb = 4;
-  for (int c = 4; c <= 16; c *= 2) {
-    if (4 * c * lpc / 64 > 16) break;
-    cb = c;
-    if ((k + c - 1) / c <= 256) break;
-  }
-  return cb;
+// Listed blocks per chunk wave: 4 up to k = 1024 (at most 256 chunks per
+// (query, head)); above, 8, or 16 when 8 would give more than 4096 chunk
+// waves in all and 16 blocks' rows fit 128 VGPRs of loads in flight (4 * 16
+// cells over 64 / lpc cells per load, at most 16 loads of keys and 16 of
+// values).  Measured with the two-workgroup merge (attention call, graph
+// replay, 4 heads): 4 blocks at k = 512 (-1.0 us fp32, -1.0 us int8 against
+// 8); at k = 2048, 8 (4 is 1 us slower for one query, 1.3-3 us for four);
+// at k = 4096 with int8 codes, 8 for one query (15.0 against 15.9 us) and 16
+// for four (23.7 against 26.0 us).  Every choice keeps nchunks within
+// kMergeMaxChunks for k <= 4096.
+int chunk_blocks(int nq, int heads, int k, int lpc) {
+  if (k <= 1024) return 4;
+  const int64_t waves8 = int64_t(nq) * heads * ((k + 7) / 8);
+  if (waves8 > 4096 && 4 * 16 * lpc / 64 <= 16) return 16;
+  return 8;
 }
 
 // Chunk partials of nq * heads * nchunks chunks from the stream's scratch.
@@ -475,7 +474,7 @@ hipError_t launch_sparse_decode_attention(const float *q, const float *kc, const
                                           int n_cells, float scale, float *out,
                                           hipStream_t stream) {
   const int lpc = dim <= 4 ? 1 : dim <= 8 ? 2 : dim <= 16 ? 4 : dim <= 32 ? 8 : dim <= 64 ? 16 : 32;
-  const int cb = chunk_blocks(k, lpc);
+  const int cb = chunk_blocks(nq, heads, k, lpc);
   int nchunks = 0;
   float *part = nullptr;
   hipError_t e = chunk_partials(stream, nq, heads, dim, k, cb, &nchunks, &part);
@@ -495,7 +494,7 @@ hipError_t launch_sparse_decode_attention_i8(const float *q, const int8_t *kq,
                                              int heads, int dim, int k, int n_cells,
                                              float scale, float *out, hipStream_t stream) {
   const int lpc = dim <= 16 ? 1 : dim <= 32 ? 2 : dim <= 64 ? 4 : 8;
-  const int cb = chunk_blocks(k, lpc);
+  const int cb = chunk_blocks(nq, heads, k, lpc);
   int nchunks = 0;
   float *part = nullptr;
   hipError_t e = chunk_partials(stream, nq, heads, dim, k, cb, &nchunks, &part);

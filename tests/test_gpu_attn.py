@@ -81,8 +81,9 @@ SHAPES = [  # nq, heads, dim, n_cells, k
     (1, 4, 128, 2048, 512), (1, 4, 128, 4001, 300), (2, 4, 128, 1000, 64), (4, 4, 128, 9000, 512),
     (1, 1, 4, 37, 9), (3, 2, 8, 50, 13), (1, 3, 16, 99, 25), (2, 2, 32, 130, 7), (1, 8, 64, 513, 8),
     (2, 2, 96, 300, 17), (8, 4, 128, 600, 129), (1, 2, 128, 5, 1), (3, 4, 64, 257, 33),
-    # chunks of 8 blocks (k in 1025..2048, or above at dim 128) and of 16 (dim 64, k > 2048)
+    # chunks of 8 blocks (k > 1024), and of 16 (more than 4096 chunk waves, dim <= 64)
     (1, 4, 128, 20000, 2000), (1, 4, 128, 17000, 3000), (2, 2, 64, 17000, 4096),
+    (3, 4, 64, 17000, 3000), (5, 4, 128, 17000, 2000),
     # the chunk-size boundaries: 256 chunks of 4 blocks, 129 of 8
     (1, 4, 128, 9000, 1024), (1, 4, 128, 9000, 1025),
 ]
@@ -186,8 +187,9 @@ SHAPES_I8 = [  # nq, heads, dim, n_cells, k
     (1, 4, 128, 2048, 512), (1, 4, 128, 4001, 300), (4, 4, 128, 9000, 512), (1, 1, 16, 37, 9),
     (3, 2, 32, 130, 13), (1, 3, 48, 99, 25), (2, 8, 64, 513, 8), (2, 2, 80, 300, 17),
     (8, 4, 96, 600, 129), (1, 2, 112, 5, 1), (3, 4, 128, 257, 33),
-    # chunks of 8 blocks (k in 1025..2048) and of 16 (k > 2048)
+    # chunks of 8 blocks (k > 1024), and of 16 (more than 4096 chunk waves)
     (1, 4, 128, 20000, 2000), (2, 4, 128, 17000, 4096), (1, 2, 48, 9000, 2049),
+    (3, 4, 128, 17000, 4096), (9, 2, 64, 9000, 2000),
 ]
 
 
