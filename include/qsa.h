@@ -189,7 +189,9 @@ int qsa_block_select(const float *q, const float *kblk, int nq, int heads, int d
  * QSA_MAX_HEAD_DIM and nq at most 65535 (else QSA_ERR_SHAPE); k in [0, QSA_TOPK_MAX_K] (else
  * QSA_ERR_K).  The cells are processed in chunks of 4, 8 or 16 listed blocks
  * (fixed by k, nq * heads and dim) and merged in chunk order, so results
- * are deterministic.  Against an FP64
+ * are deterministic for given sizes (a query's output may differ in its
+ * last bits between calls with different nq * heads, within the bound
+ * below).  Against an FP64
  * evaluation the error of out[i][h][d] stays within
  *   max|v| * (4e-6 + 24 * 2^-24 * |scale| * max_c sum_d |q[i][h][d] k[c][h][d]|)
  * over the attended cells c (fp32 rounding of the dot products, of which the
