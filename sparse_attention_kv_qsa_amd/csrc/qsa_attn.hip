@@ -50,7 +50,6 @@ namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-
 // Sum over the LPC lanes of a cell (lane bits below log2 LPC), the same tree in
 // every lane.
 template <int LPC>
@@ -76,7 +75,7 @@ __device__ __forceinline__ float group_all(float v, Op op) {
   return v;
 }
 
-constexpr int kMergeMaxChunks = 512;  // QSA_TOPK_MAX_K / 8: chunk_blocks keeps nchunks below
+constexpr int kMergeMaxChunks = 512;  // QSA_TOPK_MAX_K / 8: chunk_blocks keeps nchunks within it
 
 template <int LPC, int CB>
 __global__ __launch_bounds__(64) void attn_chunk_kernel(const float *__restrict__ q,
