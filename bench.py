@@ -21,15 +21,26 @@ Two timed passes over the same K steps:
      (qsa_block_scores, qsa_block_topk) with HIP events recorded on their
      stream around each -- per-stage times and `roofline`.  (An event costs
      a few microseconds of GPU time, so pass 1 carries none.)
-`roofline` reports the scorer (the dominant kernel) against the peak of the
-unit it runs on: fp32 MFMA with 2 * nq * A * heads * dim FLOP; bf16 MFMA on the
-exact three-way split (the prompt default), whose method forms six bf16 slice
-products per fp32 product (6 * 2 * nq * A * heads * dim FLOP), with the
-fp32-equivalent rate beside it; or HBM for the few-query dot-product kernel
-(bytes of the active summaries, the queries and the scores).
+`roofline` reports the scorer (the dominant kernel) against the peak its
+method is priced on: the algorithmic fp32 work, 2 * nq * A * heads * dim FLOP,
+against the fp32 matrix-core peak (157.3 TFLOP/s) for both matrix-core
+scorers; for the exact three-way bf16 split (the prompt default), which forms
+six bf16 slice products per fp32 product, `bf16_pipe` beside it gives that
+work (6 * 2 * nq * A * heads * dim) against the bf16 peak (2.5 PFLOP/s).  The
+few-query dot-product kernel is priced on HBM (bytes of the active summaries,
+the queries and the scores).
+
+Pass 1 is repeated (--repeats, default 7) and `stages.repeats` gives the
+median and range of the per-step time.  For a prompt workload the same run
+also times the decode call at 128K (one query, 32,770 active blocks, k = 512,
+qsa_block_select) the same way: `stages.decode_select` with its HBM fraction
+over the call's algorithmic bytes.  `fingerprints` are blake2b-64 digests of
+the host inputs and of the outputs of the first input copy.
 
 The CPU baseline is the CPU oracle (FP64 scores, then a sort-based top-k of its
-fp32-rounded scores) timed on this host's cores over the same workload.
+fp32-rounded scores) on this host: scores and top-k timed apart, once on all
+the threads of the host's share (the affinity set, capped by OMP_NUM_THREADS
+where set) over every query row, once on one thread over a sample of rows.
 
 With --attention (decode workloads, at most 8 queries) a step is the decode
 layer's whole QSA stage: the selection above, then qsa_sparse_decode_attention
@@ -91,7 +102,10 @@ def parse_args():
     p.add_argument("--scores-mode", default="auto", choices=["auto", "fp32", "bf16x3"],
                    help="precision mode of qsa_block_scores_ex (auto = the library default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-threads", type=int, default=16)
+    p.add_argument("--repeats", type=int, default=7,
+                   help="timings of the K steps (median and range in stages.repeats)")
+    p.add_argument("--no-decode-stage", action="store_true",
+                   help="prompt workloads: skip timing the 128K decode call in the same run")
     p.add_argument("--attention", action="store_true",
                    help="decode workloads: select, then attend over the selected blocks")
     p.add_argument("--pool", default="fp32", choices=["fp32", "int8"],
@@ -131,45 +145,78 @@ def read_traffic(path: str, workload: str):
         return None
 
 
-def cpu_baseline(w: synth.Workload, bt: synth.Batch, threads: int, kv=None):
-    """Time the CPU oracle on all queries of the workload, `passes` times (with
-    `kv` = (keys, values): the oracle's attention over its own selection too)."""
+def host_threads() -> tuple[int, int]:
+    """(threads of this host's share, cores in the affinity set): the affinity
+    set, capped by OMP_NUM_THREADS where the host sets it (a shared GPU host
+    gives each GPU's jobs that many threads)."""
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    share = min(avail, int(cap)) if cap.isdigit() and int(cap) > 0 else avail
+    return max(1, share), avail
+
+
+def cpu_baseline(w: synth.Workload, bt: synth.Batch, kv=None, single_rows: int = 32):
+    """Time the CPU oracle: FP64 scores, then the sort-based top-k of the
+    fp32-rounded scores (and with `kv`, the oracle's attention over that
+    selection), each step timed on its own.  Once on every thread of the
+    host's share over all query rows, once on one thread over the first
+    `single_rows` rows; three passes each, medians."""
     import oracle
 
     orc = oracle.default()
-    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    threads = max(1, min(threads, avail or 1))
-    chunks = np.array_split(np.arange(w.nq), threads)
+    threads, affinity = host_threads()
+    scale = 1.0 / np.sqrt(w.dim)
 
-    def run(rows):
-        if len(rows) == 0:
-            return
-        s64 = orc.scores_f64(bt.q[rows], bt.kblk, w.active)
-        ids = orc.topk(s64.astype(np.float32), w.k)
-        if kv is not None and len(kv) == 4:
-            orc.sparse_decode_attn_i8_f64(bt.q[rows], *kv, ids, 4 * w.active,
-                                          1.0 / np.sqrt(w.dim))
-        elif kv is not None:
-            orc.sparse_decode_attn_f64(bt.q[rows], kv[0], kv[1], ids, 4 * w.active,
-                                       1.0 / np.sqrt(w.dim))
+    def run(rows_list, pool):
+        t0 = time.perf_counter()
+        s64 = list(pool.map(lambda r: orc.scores_f64(bt.q[r], bt.kblk, w.active), rows_list))
+        t1 = time.perf_counter()
+        s32 = [a.astype(np.float32) for a in s64]
+        t2 = time.perf_counter()
+        ids = list(pool.map(lambda a: orc.topk(a, w.k), s32))
+        t3 = time.perf_counter()
+        ta = 0.0
+        if kv is not None:
+            def attend(args):
+                r, sel = args
+                if len(kv) == 4:
+                    orc.sparse_decode_attn_i8_f64(bt.q[r], *kv, sel, 4 * w.active, scale)
+                else:
+                    orc.sparse_decode_attn_f64(bt.q[r], kv[0], kv[1], sel, 4 * w.active, scale)
+            t4 = time.perf_counter()
+            list(pool.map(attend, zip(rows_list, ids)))
+            ta = time.perf_counter() - t4
+        return t1 - t0, t3 - t2, ta
 
-    passes, rates = 3, []
-    with cf.ThreadPoolExecutor(threads) as ex:
-        for _ in range(passes):
-            t0 = time.perf_counter()
-            list(ex.map(run, chunks))
-            dt = time.perf_counter() - t0
-            rates.append(w.nq * w.active / dt)
-    return {
-        "value": float(np.median(rates)),
-        "unit": UNIT,
-        "cores": threads,
+    def measure(nrows, nthreads, passes=3):
+        rows_list = [r for r in np.array_split(np.arange(nrows), nthreads) if len(r)]
+        with cf.ThreadPoolExecutor(nthreads) as ex:
+            times = [run(rows_list, ex) for _ in range(passes)]
+        ts, tk, ta = (float(np.median([t[j] for t in times])) for j in range(3))
+        units = nrows * w.active
+        out = {"value": units / (ts + tk + ta), "unit": UNIT, "cores": nthreads,
+               "scores_value": units / ts, "topk_value": units / tk,
+               "scores_ms": round(ts * 1e3, 3), "topk_ms": round(tk * 1e3, 3)}
+        if kv is not None:
+            out["attention_ms"] = round(ta * 1e3, 3)
+        return out, passes
+
+    allc, passes = measure(w.nq, min(threads, w.nq))
+    one_rows = min(single_rows, w.nq)
+    one, _ = measure(one_rows, 1)
+    steps = ("FP64 scores, then the sort top-k of the fp32-rounded scores"
+             + (", then FP64 attention over the selected blocks' cells" if kv else ""))
+    allc.update({
         "kind": "oracle",
-        "sample": (f"all {w.nq} queries x {w.active} blocks of {w.name} (FP64 scores + sort "
-                   f"top-k of the fp32-rounded scores"
-                   + (", then FP64 attention over the selected blocks' cells" if kv else "")
-                   + f"), {passes} passes, median; {threads} threads over query rows"),
-    }
+        "affinity_cores": affinity,
+        "sample": (f"all {w.nq} queries x {w.active} blocks of {w.name} ({steps}; each step "
+                   f"timed apart), {passes} passes, median; {allc['cores']} threads over query "
+                   f"rows (this host's share: {threads} of {affinity} affinity cores)"),
+        "single_thread": {**one, "rows": one_rows,
+                          "sample": f"the first {one_rows} queries of the same batch, 1 thread, "
+                                    f"{passes} passes, median"},
+    })
+    return allc
 
 
 def graph_pass(torch, step, ncopy, K, outputs):
@@ -207,6 +254,82 @@ def graph_pass(torch, step, ncopy, K, outputs):
     e1.record()
     torch.cuda.synchronize()
     return {"ms_per_step": round(e0.elapsed_time(e1) / (reps * ncopy), 5), "match": bool(match)}
+
+
+def time_steps(torch, step, ncopy, K, repeats):
+    """K steps back to back, bracketed by a device synchronisation and an
+    event pair, `repeats` times.  Returns the per-step times of the first
+    timing (wall clock, events) and of every repeat (wall clock), in ms."""
+    out = []
+    for r in range(max(1, repeats)):
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        p0.record()
+        for it in range(K):
+            step(it % ncopy)
+        p1.record()
+        torch.cuda.synchronize()
+        out.append(((time.perf_counter() - t0) * 1e3 / K, p0.elapsed_time(p1) / K))
+    return out
+
+
+def spread(ms):
+    return {"n": len(ms), "median_ms": round(float(np.median(ms)), 5),
+            "min_ms": round(float(np.min(ms)), 5), "max_ms": round(float(np.max(ms)), 5)}
+
+
+def select_bytes(w) -> float:
+    """Algorithmic bytes of one select call: the active summaries and the
+    queries read, the scores written and read back, the ids written."""
+    return 4.0 * (w.active * w.K + w.nq * w.K + 2 * w.nq * w.active + w.nq * w.k)
+
+
+def decode_stage(torch, args, ncopy):
+    """The decode call at 128K in the same run: K select calls back to back
+    (repeated), and the same calls replayed from a captured graph."""
+    from sparse_attention_kv_qsa_amd import qsa_block_select
+
+    wd = synth.WORKLOADS["decode-128k"]
+    bt = synth.make_batch(wd)
+    dev = torch.device("cuda:0")
+    q = [torch.from_numpy(bt.q).to(dev) for _ in range(ncopy)]
+    kb = [torch.from_numpy(bt.kblk).to(dev) for _ in range(ncopy)]
+    sc = [torch.empty((wd.nq, wd.active), dtype=torch.float32, device=dev) for _ in range(ncopy)]
+    ids = [torch.empty((wd.nq, wd.k), dtype=torch.int32, device=dev) for _ in range(ncopy)]
+
+    def step(c):
+        qsa_block_select(q[c], kb[c], wd.k, wd.active, scores=sc[c], ids=ids[c])
+
+    for it in range(max(args.warmup, 2 * ncopy)):
+        step(it % ncopy)
+    torch.cuda.synchronize()
+    K = max(args.steps, 2 * ncopy)
+    reps = time_steps(torch, step, ncopy, K, args.repeats)
+    wall = [r[0] for r in reps]
+    graph = graph_pass(torch, step, ncopy, K, [ids, sc])
+    nbytes = select_bytes(wd)
+    med = float(np.median(wall)) * 1e-3
+    g = graph["ms_per_step"] * 1e-3
+    out = {
+        "workload": (f"{wd.name}: {wd.nq} query x {wd.active} active blocks "
+                     f"({wd.capacity}-block capacity), {wd.heads} heads x {wd.dim}, k={wd.k}"),
+        "call": "qsa_block_select",
+        "algorithmic_bytes": int(nbytes),
+        "us_per_call": round(med * 1e6, 2),
+        "repeats": spread(wall),
+        "hbm_gbs": round(nbytes / med / 1e9, 1),
+        "hbm_frac": round(nbytes / med / 1e9 / PEAK_HBM_GBS, 4),
+        "graph_us_per_call": round(g * 1e6, 2),
+        "graph_hbm_frac": round(nbytes / g / 1e9 / PEAK_HBM_GBS, 4),
+        "graph_replays_match_eager": graph["match"],
+        "target_hbm_frac": 0.60,
+        "fingerprints": {"q": synth.fingerprint(bt.q), "kblk": synth.fingerprint(bt.kblk),
+                         "ids": synth.fingerprint(ids[0].cpu().numpy())},
+    }
+    del q, kb, sc, ids
+    torch.cuda.synchronize()
+    return out
 
 
 def main():
@@ -295,46 +418,30 @@ def main():
         step(it % ncopy)
     torch.cuda.synchronize()
 
-    # Pass 1: throughput of the hot path.
+    # Pass 1: throughput of the hot path, K steps, then repeated.
     K = args.steps
-    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    p0.record()
-    for it in range(K):
-        step(it % ncopy)
-    p1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / K
-    value = w.nq * w.active / (wall / K)
-    gpu_ms_step = p0.elapsed_time(p1) / K
+    first = time_steps(torch, step, ncopy, K, 1)[0]
+    ms_step, gpu_ms_step = first
+    value = w.nq * w.active / (ms_step * 1e-3)
+    reps = [ms_step] + [r[0] for r in time_steps(torch, step, ncopy, K, args.repeats - 1)] \
+        if args.repeats > 1 else [ms_step]
 
-    # Pass 2: per-kernel durations, events around the two separate calls.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    torch.cuda.synchronize()
-    for it in range(K):
-        c = it % ncopy
-        e0, e1, e2 = ev[it]
-        e0.record()
-        qsa_block_scores_ex(q_d[c], k_d[c], w.active, scores=s_d[c], mode=mode)
-        e1.record()
-        qsa_block_topk(s_d[c], w.k, ids=i_d[c])
-        e2.record()
-    torch.cuda.synchronize()
-    score_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
-    topk_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    # Pass 2: the two calls apart, each as K calls replayed from a captured
+    # graph between one event pair (per-call time on the stream, kernel plus
+    # the gap to the next; no host cost and no per-call events).
+    gs = graph_pass(torch, lambda c: qsa_block_scores_ex(q_d[c], k_d[c], w.active,
+                                                         scores=s_d[c], mode=mode),
+                    ncopy, K, [s_d])
+    gt = graph_pass(torch, lambda c: qsa_block_topk(s_d[c], w.k, ids=i_d[c]), ncopy, K, [i_d])
+    score_ms, topk_ms = gs["ms_per_step"], gt["ms_per_step"]
 
     attn_ms = None
     if attn:
         # Pass 2b: the attention call alone (the ids of every copy were
         # written by the passes above), K calls replayed from a captured
-        # graph between one event pair: the per-call time on the stream, both
-        # kernels and the gap between them included.  Launched one by one
-        # from Python, a call this short would time the binding's host cost
-        # instead; an event pair per call would add its own microseconds.
+        # graph between one event pair.
         ga = graph_pass(torch, attend, ncopy, K, [o_d])
-        attn_ms = [ga["ms_per_step"]]
+        attn_ms = ga["ms_per_step"]
         attn_graph_ok = ga["match"]
 
     graph = None
@@ -342,38 +449,39 @@ def main():
         graph = graph_pass(torch, step, ncopy, K,
                            [i_d] + ([o_d] if attn else []))
 
-    flop = 2.0 * w.nq * w.active * w.K  # fp32-equivalent FLOP of the scores
-    score_avg_s = float(np.mean(score_ms)) * 1e-3
+    fingerprints = {"q": synth.fingerprint(bt.q), "kblk": synth.fingerprint(bt.kblk),
+                    "scores": synth.fingerprint(s_d[0].cpu().numpy()),
+                    "ids": synth.fingerprint(i_d[0].cpu().numpy())}
+
+    flop = 2.0 * w.nq * w.active * w.K  # algorithmic fp32 FLOP of the scores
+    score_s = score_ms * 1e-3
     # The kernel the library runs for this shape and mode (mirrors its dispatch).
     gemv_ok = w.nq <= 8 and w.nq * -(-w.K // 256) <= 16
     if gemv_ok and mode != "bf16x3":
         path = "gemv"
     else:
         path = "bf16x3" if mode in ("auto", "bf16x3") else "fp32"
-    extra = {}
-    select_bytes = 4.0 * (w.active * w.K + w.nq * w.K + 2 * w.nq * w.active + w.nq * w.k)
     if path == "gemv":
         nbytes = 4.0 * (w.active * w.K + w.nq * w.K + w.nq * w.active)
-        gbs = nbytes / score_avg_s / 1e9
+        gbs = nbytes / score_s / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": "scores_gemv_kernel"}
-    elif path == "fp32":
-        tf = flop / score_avg_s / 1e12
+                "kernel": "scores_gemv_kernel", "bytes_per_launch": int(nbytes),
+                "ms_per_launch": round(score_ms, 5)}
+    else:
+        tf = flop / score_s / 1e12
         roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_MFMA_TFLOPS, 4),
-                "traffic": read_traffic("fp32", w.name), "kernel": "scores_mfma_kernel"}
-    else:
-        # The split method forms six bf16 slice products per fp32 product: its
-        # algorithmic work on the bf16 matrix cores is 6 * 2 * nq * A * K.
-        tf = 6.0 * flop / score_avg_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_MFMA_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_MFMA_TFLOPS, 4),
-                "traffic": read_traffic("bf16x3", w.name), "kernel": "scores_bf16x3_kernel"}
-        extra = {"scores_fp32_equiv_tflops": round(flop / score_avg_s / 1e12, 2),
-                 "scores_frac_of_fp32_mfma_peak": round(flop / score_avg_s / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)}
+                "traffic": read_traffic(path, w.name),
+                "kernel": "scores_mfma_kernel" if path == "fp32" else "scores_bf16x3_kernel",
+                "flop_per_launch": int(flop), "ms_per_launch": round(score_ms, 5)}
+        if path == "bf16x3":
+            # The split forms six bf16 slice products per fp32 product.
+            roof["bf16_pipe"] = {"achieved": round(6 * tf, 2), "peak": PEAK_BF16_MFMA_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(6 * tf / PEAK_BF16_MFMA_TFLOPS, 4),
+                                 "flop_per_launch": int(6 * flop)}
     topk_bytes = 4.0 * (w.nq * w.active + w.nq * w.k)
-    topk_avg_s = float(np.mean(topk_ms)) * 1e-3
+    sbytes = select_bytes(w)
 
     out = {
         "metric": METRIC,
@@ -399,18 +507,19 @@ def main():
         },
         "stages": {
             "gpu_ms_per_step": round(gpu_ms_step, 5),
-            "step_hbm_gbs": round(select_bytes / (ms_step * 1e-3) / 1e9, 1),
-            "step_hbm_frac": round(select_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "scores_ms": round(float(np.mean(score_ms)), 5),
-            "scores_ms_median": round(float(np.median(score_ms)), 5),
-            "topk_ms": round(float(np.mean(topk_ms)), 5),
-            "topk_ms_median": round(float(np.median(topk_ms)), 5),
-            "topk_gbs": round(topk_bytes / topk_avg_s / 1e9, 1),
-            "topk_hbm_frac": round(topk_bytes / topk_avg_s / 1e9 / PEAK_HBM_GBS, 4),
+            "repeats": spread(reps),
+            "step_hbm_gbs": round(sbytes / (ms_step * 1e-3) / 1e9, 1),
+            "step_hbm_frac": round(sbytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "scores_ms": round(score_ms, 5),
+            "topk_ms": round(topk_ms, 5),
+            "stage_timing": "each call K times from a replayed graph, one event pair",
+            "stage_graphs_match_eager": bool(gs["match"] and gt["match"]),
+            "topk_gbs": round(topk_bytes / (topk_ms * 1e-3) / 1e9, 1),
+            "topk_hbm_frac": round(topk_bytes / (topk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "scores_kernel": path,
-            **extra,
         },
         "roofline": roof,
+        "fingerprints": fingerprints,
         "cpu_baseline": None,
     }
     if graph is not None:
@@ -422,8 +531,7 @@ def main():
         gathered = (2.0 * w.nq * w.k * 4 * (w.K + 2 * w.heads) if int8 else
                     2.0 * w.nq * w.k * 4 * w.K * 4)
         abytes = gathered + 4.0 * (2 * w.nq * w.K + w.nq * w.k)
-        a_avg_s = float(np.mean(attn_ms)) * 1e-3
-        gbs = abytes / a_avg_s / 1e9
+        gbs = abytes / (attn_ms * 1e-3) / 1e9
         out["metric"] = ("QSA decode layer: select + block-sparse attention over the "
                          "selected blocks; queries*blocks/s")
         out["vs_baseline"] = None
@@ -434,7 +542,7 @@ def main():
         out["data"] += ("; int8 key/value codes round(N(0,40)) with binary16 scales in "
                         "[0.01, 0.04], NaN scales past the active blocks" if int8 else
                         "; N(0,1) fp32 key/value cells, NaN past the active blocks")
-        out["stages"]["attention_ms"] = round(float(np.mean(attn_ms)), 5)
+        out["stages"]["attention_ms"] = round(attn_ms, 5)
         out["stages"]["attention_graph_replays_match_eager"] = attn_graph_ok
         out["roofline_attention"] = {
             "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -442,8 +550,11 @@ def main():
             "bytes_per_call": int(abytes),
             "kernel": ("attn_chunk_i8_kernel" if int8 else "attn_chunk_kernel")
             + " + attn_merge_kernel (one call)"}
+    if w.nq > 8 and not attn and not args.no_decode_stage:
+        del s_d, i_d
+        out["stages"]["decode_select"] = decode_stage(torch, args, ncopy)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, bt, args.cpu_threads, kv if attn else None)
+        out["cpu_baseline"] = cpu_baseline(w, bt, kv if attn else None)
     print(json.dumps(out), flush=True)
 
 

@@ -18,18 +18,31 @@
  *      count, never the capacity).
  *
  * Conventions for every entry point:
- *   - Every data pointer is a DEVICE pointer on the current HIP device, owned
- *     by the caller.  Some launches also need device scratch (the published
- *     group words of the few-row top-k and of the fused decode select, the
- *     chunk partials of the decode attention); the library keeps one scratch
- *     buffer per (device, stream),
- *     allocated with hipMalloc on first need, grown when a call needs more
- *     and never freed before the process ends.  Work on one stream runs in
- *     order, so calls on the same stream share it safely; calls on different
- *     streams use different buffers.  The first call of a given size on a
- *     stream may therefore allocate: make it before capturing that stream
- *     into a HIP graph.  The library may be called from several host threads
- *     at once.
+ *   - Every data pointer is a DEVICE pointer on the device of `stream`, owned
+ *     by the caller.
+ *   - Device scratch.  Some launches need device memory beyond the caller's
+ *     buffers: the published group words of the few-row top-k and of the
+ *     fused decode select (at most 128 KB per query row), and the chunk
+ *     partials of the decode attention (nq * heads * ceil(k/4) * (dim + 4)
+ *     floats at most).  The library keeps one scratch buffer per (device,
+ *     stream handle), allocated with hipMalloc on first need, grown when a
+ *     call needs more and never freed before the process ends.  Work on one
+ *     stream runs in order, so calls on the same stream share it safely;
+ *     calls on different streams use different buffers.
+ *       May allocate (the first call of a given size on a stream):
+ *         qsa_block_topk             when 1 <= nq <= QSA_TOPK_FEW_ROWS, k >= 1 and active_blocks >= 1;
+ *         qsa_block_select           under the same condition;
+ *         qsa_sparse_decode_attention, qsa_sparse_decode_attention_i8
+ *                                    whenever nq >= 1 and heads >= 1.
+ *       Never allocate: qsa_block_scores, qsa_block_scores_ex, and
+ *         qsa_block_topk / qsa_block_select with nq > QSA_TOPK_FEW_ROWS.
+ *     Consequences: make one call of each size on a stream before capturing
+ *     that stream into a HIP graph (an allocation during capture fails with
+ *     QSA_ERR_NOMEM or QSA_ERR_LAUNCH); and synchronise a stream before
+ *     destroying it, because the buffer is keyed on the stream handle: if
+ *     the runtime hands the handle of a destroyed stream to a new one while
+ *     work that uses the buffer is still queued, the two would share it.
+ *     The library may be called from several host threads at once.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *     void*; NULL = the default stream).  The call returns once the work is
  *     enqueued; results are valid after the stream is synchronised.
@@ -191,11 +204,16 @@ int qsa_block_select(const float *q, const float *kblk, int nq, int heads, int d
  * (fixed by k, nq * heads and dim) and merged in chunk order, so results
  * are deterministic for given sizes (a query's output may differ in its
  * last bits between calls with different nq * heads, within the bound
- * below).  Against an FP64
- * evaluation the error of out[i][h][d] stays within
- *   max|v| * (4e-6 + 24 * 2^-24 * |scale| * max_c sum_d |q[i][h][d] k[c][h][d]|)
- * over the attended cells c (fp32 rounding of the dot products, of which the
- * second term bounds the effect on the softmax weights).
+ * below).  Against an FP64 evaluation the error of out[i][h][d] stays within
+ *   max|v| * (T + 2 n_s 2^-24 |scale| max_c sum_d |q[i][h][d] k[c][h][d]|)
+ * over the attended cells c, where n_s = 5 + log2(LPC) roundings per score
+ * (LPC = dim/4 rounded up to a power of two) and T is a first-order bound
+ * over the kernels' own summation sequences: in units of 2^-24,
+ *   T = 2 (R + log2(64/LPC)) + min(n, 32) + 2 ceil(n/32) + 6 + 2 (8 + ln 4k)
+ * for chunks of CB listed blocks (CB = 4 up to k = 1024, else 8 or 16;
+ * R = 4 CB LPC / 64 cell rows per lane, n = ceil(k / CB) chunks), which
+ * assumes expf within 2 ulp.  At dim 128 T runs from 2.7e-6 (k = 1) to
+ * 8.3e-6 (k = 4096).
  * nq == 0 or heads == 0 is a successful no-op.
  */
 #define QSA_ATTN_MAX_DIM 128
@@ -222,7 +240,8 @@ int qsa_sparse_decode_attention(const float *q, const float *kcache, const float
  * QSA_ERR_SHAPE); other limits and errors as above.  The kernel forms
  * scale * (kscale * sum_d q_d kcode_d) and sums (w * vscale) * vcode in fp32;
  * against an FP64 evaluation on the dequantised rows the error stays within
- *   max|v| * (8e-6 + 48 * 2^-24 * |scale| * max_c sum_d |q[i][h][d] k[c][h][d]|).
+ * the bound above with n_s = 18 + log2(LPC), LPC = dim/16 rounded up to a
+ * power of two, and one more rounding per value term (w * vscale).
  * A cell costs 2 * (dim + 2) bytes per head to read instead of 8 * dim.
  */
 int qsa_sparse_decode_attention_i8(const float *q, const int8_t *kcode, const uint16_t *kscale,

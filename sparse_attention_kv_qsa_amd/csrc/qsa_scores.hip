@@ -35,6 +35,20 @@ __device__ __forceinline__ f4 load_f4_stream(const float *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const f4 *>(p));
 }
 
+// Sum over the 64 lanes by an XOR butterfly (strides 32, 16, ..., 1): every
+// lane adds the same two values in the same order at each level, so all lanes
+// end with the bitwise-same sum.  The exchanges are lane swaps and DPP moves,
+// not LDS permutes.
+__device__ __forceinline__ float butterfly_sum(float v) {
+  v += __uint_as_float(lane_xor<32>(__float_as_uint(v)));
+  v += __uint_as_float(lane_xor<16>(__float_as_uint(v)));
+  v += __uint_as_float(lane_xor<8>(__float_as_uint(v)));
+  v += __uint_as_float(lane_xor<4>(__float_as_uint(v)));
+  v += __uint_as_float(lane_xor<2>(__float_as_uint(v)));
+  v += __uint_as_float(lane_xor<1>(__float_as_uint(v)));
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // GEMV scorer: NQ queries (padded), NC float4 chunks of K per lane, U rows per
 // wave.  Lane l owns elements [4*(c*64 + l), +4) of every row for c < NC.
@@ -84,9 +98,7 @@ __global__ __launch_bounds__(256) void scores_gemv_kernel(const float *__restric
         acc = __builtin_fmaf(qf[n][c].z, kf[u][c].z, acc);
         acc = __builtin_fmaf(qf[n][c].w, kf[u][c].w, acc);
       }
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-      p[u][n] = acc;
+      p[u][n] = butterfly_sum(acc);
     }
 
 #pragma unroll
@@ -109,9 +121,16 @@ __global__ __launch_bounds__(256) void scores_gemv_kernel(const float *__restric
 // ---------------------------------------------------------------------------
 // Eight waves per SIMD when the registers allow (at most 64 VGPRs): with
 // 16-wave workgroups one per CU would leave the CU idle through each
-// workgroup's barrier and sort.
+// workgroup's barrier and sort.  The widest rows (NC = 16: a query and a
+// summary row of 4096 floats, 128 VGPRs of operands) take 8-wave workgroups
+// at two waves per SIMD, so nothing spills.
 template <int NQ, int NC, int U, int NW>
-__global__ __launch_bounds__(64 * NW, ((NQ + U) * NC <= 10 ? 8 : 4)) void scores_gemv_tops_kernel(const float *__restrict__ q,
+constexpr int gemv_tops_min_waves() {
+  return (NQ + U) * NC <= 10 ? 8 : NC >= 16 ? 2 : 4;
+}
+
+template <int NQ, int NC, int U, int NW>
+__global__ __launch_bounds__(64 * NW, (gemv_tops_min_waves<NQ, NC, U, NW>())) void scores_gemv_tops_kernel(const float *__restrict__ q,
                                                                 const float *__restrict__ kblk,
                                                                 int nq, int K, int A,
                                                                 float *__restrict__ scores,
@@ -156,8 +175,7 @@ __global__ __launch_bounds__(64 * NW, ((NQ + U) * NC <= 10 ? 8 : 4)) void scores
           acc = __builtin_fmaf(qf[n][c].z, kf[u][c].z, acc);
           acc = __builtin_fmaf(qf[n][c].w, kf[u][c].w, acc);
         }
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+        acc = butterfly_sum(acc);
         const int64_t r = row0 + u;
         if (lane == u * NQ + n && r < A && n < nq) scores[int64_t(n) * A + r] = acc;
         if (lane == 0) sc[n][wave * RPW + it * U + u] = acc;
@@ -181,8 +199,10 @@ hipError_t launch_gemv_tops_nc(const float *q, const float *kblk, int nq, int K,
   // waves per 64-block group: 16 (four rows each) for one or two queries;
   // 8 (eight rows each, half the registers per workgroup, so the barrier and
   // the sort of one workgroup stall fewer waves) from four queries on
-  // (measured: 4 queries 29.4 -> 27.2 us per select; 1 and 2 slower).
-  constexpr int NW = NQ >= 4 ? 8 : 16;
+  // (measured: 4 queries 29.4 -> 27.2 us per select; 1 and 2 slower), and for
+  // 4096-float rows, whose operands need more than the 128 VGPRs of four
+  // waves per SIMD.
+  constexpr int NW = (NQ >= 4 || NC >= 16) ? 8 : 16;
   scores_gemv_tops_kernel<NQ, NC, U, NW><<<ngroups, 64 * NW, 0, stream>>>(q, kblk, nq, K, A, scores, tops,
                                                                  ngroups, M);
   return hipGetLastError();

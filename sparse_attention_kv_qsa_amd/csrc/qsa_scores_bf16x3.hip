@@ -157,18 +157,21 @@ __device__ __forceinline__ void split_tile(const float *__restrict__ q,
   // QD (K a multiple of 32): the wave's 32 query rows of a step go global ->
   // LDS by direct loads, 8 lanes per 128-byte row segment, piece p of row r
   // at slot p ^ ((r >> 1) & 7); the lanes then read their MFMA slices.
-  uint32_t dq[4];
+  // Row 8i + lane/8 of the wave: the swizzle depends on i only through its
+  // parity, so two lane offsets serve the four loads and the row step 8i goes
+  // into the scalar offset.
+  uint32_t dq[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
     const int r = 8 * i + (lane >> 3);
     const int p = (lane & 7) ^ ((r >> 1) & 7);
-    dq[i] = uint32_t(32 * wave + r) * row_bytes + uint32_t(p) * 16u;
+    dq[i] = uint32_t(32 * wave + (lane >> 3)) * row_bytes + uint32_t(p) * 16u;
   }
   auto dma_q = [&](int buf, int kk) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(qst + buf * 256 + i * 64), 16, dq[i],
-                                               kk * 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(qst + buf * 256 + i * 64), 16, dq[i & 1],
+                                               kk * 4 + 8 * i * int(row_bytes), 0, 0);
   };
   auto read_q = [&](int buf) {
 #pragma unroll
@@ -390,29 +393,33 @@ __device__ __forceinline__ void split_tail(const float *__restrict__ q,
 // of one block tile adjacent) and every eighth ragged unit, ragged first.  A
 // ragged unit is a 64-query split_tail tile when the ragged column has at
 // most 32 active blocks (narrow), else a 128-query split_tile<false> tile.
-__global__ __launch_bounds__(256, 2) void scores_bf16x3_kernel(const float *__restrict__ q,
+// QD (K a multiple of 32, every workload here) stages the query rows through
+// LDS with direct loads and runs at two waves per SIMD; the other K take the
+// register-loaded queries in an instance of their own with the whole
+// register file per wave, so neither instance spills.
+template <bool QD>
+__global__ __launch_bounds__(256, QD ? 2 : 1) void scores_bf16x3_kernel(const float *__restrict__ q,
                                                                const float *__restrict__ kblk,
                                                                int nq, int K, int A,
                                                                float *__restrict__ scores,
                                                                int nqt, int nct, int ntail,
                                                                int narrow) {
   __shared__ u4 bl[2 * 3 * 2 * 2 * 64];  // 24 KB: two steps x three planes x (2 K halves x 2 column halves x 64 lanes)
-  __shared__ u4 qst[4 * 2 * 256];       // 32 KB: per wave, two steps of 32 query rows x 128 bytes
+  __shared__ u4 qst[QD ? 4 * 2 * 256 : 1];  // 32 KB: per wave, two steps of 32 query rows x 128 bytes
   const int x = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
+  u4 *mq = qst + (QD ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 512 : 0);
   const int tails_here = ntail > x ? (ntail - x + 7) / 8 : 0;
   if (slot < tails_here) {
     const int u = x + 8 * slot;  // ragged unit
     if (narrow) split_tail(q, kblk, nq, K, A, scores, u * BT, (nct - 1) * BN, bl);
-    else split_tile<false, false>(q, kblk, nq, K, A, scores, u * BM, (nct - 1) * BN, bl, qst);
+    else split_tile<false, QD>(q, kblk, nq, K, A, scores, u * BM, (nct - 1) * BN, bl, mq);
     return;
   }
   const int64_t nfull = int64_t(nqt) * (nct - (ntail > 0 ? 1 : 0));
   const int64_t f = nfull * x / 8 + (slot - tails_here);
   if (f >= nfull * (x + 1) / 8) return;  // whole workgroup leaves before any barrier
-  u4 *mq = qst + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 512;
-  if (K % BK == 0) split_tile<true, true>(q, kblk, nq, K, A, scores, int(f % nqt) * BM, int(f / nqt) * BN, bl, mq);
-  else split_tile<true, false>(q, kblk, nq, K, A, scores, int(f % nqt) * BM, int(f / nqt) * BN, bl, mq);
+  split_tile<true, QD>(q, kblk, nq, K, A, scores, int(f % nqt) * BM, int(f / nqt) * BN, bl, mq);
 }
 
 }  // namespace
@@ -430,8 +437,12 @@ hipError_t launch_block_scores_bf16x3(const float *q, const float *kblk, int nq,
     const int64_t tails = ntail > x ? (ntail - x + 7) / 8 : 0;
     per = std::max(per, tails + nfull * (x + 1) / 8 - nfull * x / 8);
   }
-  scores_bf16x3_kernel<<<int(8 * per), 256, 0, stream>>>(q, kblk, nq, K, A, scores, nqt, nct,
-                                                         ntail, narrow);
+  if (K % BK == 0)
+    scores_bf16x3_kernel<true><<<int(8 * per), 256, 0, stream>>>(q, kblk, nq, K, A, scores, nqt,
+                                                                 nct, ntail, narrow);
+  else
+    scores_bf16x3_kernel<false><<<int(8 * per), 256, 0, stream>>>(q, kblk, nq, K, A, scores, nqt,
+                                                                  nct, ntail, narrow);
   return hipGetLastError();
 }
 

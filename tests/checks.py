@@ -17,31 +17,73 @@ from __future__ import annotations
 import numpy as np
 
 # Decode attention gate, per query i and head h:
-#   max_d |out - out64| <= max_{c} |v[c][h]| * (ATTN_TOL + ATTN_SCORE_TOL * scale * max_c sum_d |q_d k_cd|)
-# over the attended cells c.  The output is a convex combination of value
-# rows.  An fp32 score s_c = scale * q.k_c carries at most about
-# (4 + log2(dim/4)) * 2^-24 * scale * sum_d |q_d k_cd| of rounding (a 4-term
-# FMA chain and a fixed lane tree, <= 9 levels at dim 128); an error e in
-# every score moves the normalised weights by at most ~2e relatively, hence
-# the second term with ATTN_SCORE_TOL = 2 * 12 * 2^-24 (margin included).
-# The weighted sums (<= 16 terms per lane, then a lane tree of <= 6 levels),
-# the chunk merge (<= 32 chunks in sequence per wave, <= 16 wave sums in
-# sequence) and exp add a few 2^-24 of max|v| (a convex combination), bounded
-# by ATTN_TOL = 4e-6 at the sizes tested.
-ATTN_TOL = 4e-6
-ATTN_SCORE_TOL = 2 * 12 * 2.0 ** -24
-# The int8 pool, gated on its dequantised rows: a lane's score sums 16
-# code products in one FMA chain, then a lane tree of <= 3 levels and two
-# multiplications (key scale, then scale): <= 21 roundings, 24 with margin,
-# doubled as above.  The value sums take one more rounding per term (w times
-# the value scale): ATTN_I8_TOL = 2 * ATTN_TOL.
-ATTN_I8_TOL = 8e-6
-ATTN_I8_SCORE_TOL = 2 * 24 * 2.0 ** -24
+#   max_d |out - out64| <= max_c |v[c][h]| * (T + S * |scale| * max_c sum_d |q_d k_cd|)
+# over the attended cells c, with T and S from attn_tols(k, dim).  A first-order
+# rounding bound (u = 2^-24, every count below times u; n*u < 1e-3 throughout,
+# so the second-order terms are far below the margin).  The kernels' sequences:
+#
+# * score of a cell (S): a lane's 4-term FMA chain (4 roundings on the first
+#   product), a tree over the LPC lanes of the row (log2 LPC), the scale (1):
+#   n_s = 5 + log2 LPC roundings of at most sum_d |q_d k_cd| each.  Score errors
+#   up to e move the normalised weights by e relatively, on both the sum and
+#   the normaliser: S = 2 * n_s * u.  int8 pool: 16 products in one chain,
+#   log2 LPC, the key scale and the scale: n_s = 18 + log2 LPC.
+# * T, the rest, for the worst chunk size the kernel may pick at this k (4
+#   listed blocks up to k = 1024, else 8 or 16; R = 4 * CB / CPI rows per
+#   lane, CPI = 64 / LPC cells per load, nch = ceil(k / CB) chunks,
+#   nw = ceil(nch / 32) merge waves):
+#     value sum in a chunk      R + log2 CPI   (+1 for int8: w * value scale)
+#     weight sum in a chunk     R + log2 CPI
+#     merge of the value sums   min(nch, 32) + nw - 1   (FMA chain per wave, then the waves in order)
+#     merge of the weight sums  1 + 6 + nw - 1          (product, 64-lane tree, the waves)
+#     the division              1
+#     the weights themselves    2 * (2 * 2 ulp of exp + ln(4k))  (exp(s - m_j) * exp(m_j - M) as
+#                               computed has relative error u*|s - M| + 2 ulps of each exp; the
+#                               mean of |s - M| under the softmax weights is at most the log of
+#                               the cell count; a weight error moves both sum and normaliser)
+#   Each bounded against sum_c W_c |v_c| <= max|v| * sum_c W_c.  The exp
+#   accuracy (2 ulp, 2^-22 relative) is the one assumption not read off the
+#   kernel's own sequence.
+_U = 2.0 ** -24
 
 
-def attn_limit(q, kc, vc, ids, n_cells, scale, tol=ATTN_TOL, score_tol=ATTN_SCORE_TOL):
-    """The gate above for every (query, head): an array [nq][heads]."""
-    nq, heads, _ = q.shape
+def _lpc(dim: int, int8: bool) -> int:
+    per = 16 if int8 else 4                 # elements per lane
+    lpc = 1
+    while lpc * per < dim:
+        lpc *= 2
+    return lpc
+
+
+def attn_tols(k: int, dim: int, int8: bool = False) -> tuple[float, float]:
+    """(T, S) of the gate above for a call with k listed blocks and this dim."""
+    import math
+    lpc = _lpc(dim, int8)
+    cpi = 64 // lpc
+    n_s = (18 if int8 else 5) + int(math.log2(lpc))
+    worst = 0.0
+    for cb in ([4] if k <= 1024 else [8, 16]):
+        rounds = max(1, 4 * cb // cpi)
+        if rounds > 16:
+            continue                        # more rows than the kernel holds: never chosen
+        n_chunk = rounds + int(math.log2(cpi))
+        nch = -(-max(k, 1) // cb)
+        nw = -(-nch // 32)
+        n = ((n_chunk + (1 if int8 else 0))   # value sums in the chunk
+             + n_chunk                        # weight sums in the chunk
+             + min(nch, 32) + nw - 1          # merge of the value sums
+             + 1 + 6 + nw - 1                 # merge of the weight sums
+             + 1                              # division
+             + 2 * (2 * 4 + math.log(4 * max(k, 1))))  # the weights
+        worst = max(worst, n)
+    return worst * _U, 2 * n_s * _U
+
+
+def attn_limit(q, kc, vc, ids, n_cells, scale, int8: bool = False):
+    """The gate above for every (query, head): an array [nq][heads].  For the
+    int8 pool, kc and vc are the dequantised rows (code * scale)."""
+    nq, heads, dim = q.shape
+    tol, score_tol = attn_tols(ids.shape[1], dim, int8)
     lim = np.zeros((nq, heads))
     for i in range(nq):
         cells = [4 * b + e for b in ids[i] if b >= 0 for e in range(4) if 4 * b + e < n_cells]

@@ -238,6 +238,25 @@ def test_topk_clustered(a, k, path):
     assert ids.shape[1] == k
 
 
+# Long rows on the few-row path: groups of 256 elements (rows of 131,073 to
+# 524,288 blocks) and of 1,024 (524,289 to 2,097,152), and past that the
+# streaming one-workgroup path.  Heavy-tie rows make nearly every group
+# "rich" (more than 1,024 of them at these lengths), so the exact
+# one-workgroup fallback runs from the grouped launch as well.
+LONG_CASES = [(131073, 64), (300000, 512), (524288, 4096), (524289, 64), (600000, 1024),
+              (2000000, 4096), (2097152, 300), (2097153, 512)]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("a,k", LONG_CASES)
+def test_topk_long_rows(a, k):
+    rng = np.random.default_rng(a + 7 * k)
+    print(f"\n[long rows] A={a} k={k}", flush=True)
+    check_topk((rng.standard_normal((2, a)) * 20).astype(np.float32), k)
+    check_topk(tie_rows(rng, 2, a, 7), k)
+    check_topk(clustered_rows(rng, a), k)
+
+
 @pytest.mark.parametrize("nq", [1, 2, 5, 16, 17, 40])
 def test_topk_batch_sizes(nq):
     # around the switch between the two paths

@@ -150,6 +150,42 @@ def pin_topk_lexsort(orc):
     return None
 
 
+def pin_topk_f64_lexsort(orc):
+    """The FP64 selection (a diagnostic: how often the fp32 scores select what
+    the FP64 ones do) against numpy lexsort on float64 rows whose values differ
+    only below fp32 precision: neighbours one FP64 ulp apart, values split by
+    2^-40 relative, exact ties, signed zeros and infinities.  A NaN must be
+    reported."""
+    rng = np.random.default_rng(12)
+    for a, k in [(64, 10), (500, 77), (2000, 300), (37, 50)]:
+        base = np.round(rng.standard_normal(a) * 3)
+        jitter = rng.integers(-2, 3, a).astype(np.float64)
+        rows = [
+            base + jitter * 2.0 ** -40 * np.maximum(np.abs(base), 1.0),      # below fp32's ulp
+            np.where(rng.random(a) < 0.5, base, np.nextafter(base, np.inf)),  # one FP64 ulp apart
+            np.where(rng.random(a) < 0.3, -0.0, np.where(rng.random(a) < 0.5, 0.0, base)),
+            np.where(rng.random(a) < 0.05, np.inf, np.where(rng.random(a) < 0.05, -np.inf, base)),
+        ]
+        s = np.ascontiguousarray(np.stack(rows))
+        got = orc.topk_f64(s, k)
+        for i in range(len(rows)):
+            order = np.lexsort((np.arange(a), -s[i]))[: min(k, a)]
+            want = np.full(k, -1, np.int64)
+            want[: len(order)] = order
+            if not np.array_equal(got[i], want):
+                return f"FP64 lexsort a={a} k={k} row {i}"
+    # narrowing to fp32 would merge the first row's neighbours into ties
+    near = np.array([[1.0, 1.0 + 2.0 ** -40, 1.0 + 2.0 ** -41]])
+    if orc.topk_f64(near, 3)[0].tolist() != [1, 2, 0]:
+        return "FP64 selection lost differences below fp32 precision"
+    bad = np.array([[0.5, np.nan, 1.0]])
+    try:
+        orc.topk_f64(bad, 2)
+    except oracle.OracleError:
+        return None
+    return "a NaN FP64 score was not reported"
+
+
 def pin_topk_special_rows(orc):
     a, k = 37, 9
     const = np.full((1, a), 3.5, np.float32)
@@ -374,7 +410,7 @@ def pin_attn_i8_single_cell(orc):
 
 
 PINS = [pin_hand_example, pin_integer_exact, pin_float64_matmul, pin_exact_rationals,
-        pin_topk_brute_force, pin_topk_lexsort, pin_topk_special_rows,
+        pin_topk_brute_force, pin_topk_lexsort, pin_topk_f64_lexsort, pin_topk_special_rows,
         pin_topk_invariants, pin_active_rows_only, pin_attn_single_cell,
         pin_attn_uniform_weights, pin_attn_numpy, pin_attn_two_cells_closed_form,
         pin_attn_invariants, pin_half_decoding, pin_attn_i8_dequantized,
@@ -418,6 +454,7 @@ def test_infinities_order_naturally():
 
 
 def test_f64_selection_matches_fp32_on_exact_values():
+    # consistency only (both share the sort); pin_topk_f64_lexsort is the pin
     rng = np.random.default_rng(9)
     s = np.round(rng.standard_normal((4, 300)) * 8)
     assert np.array_equal(ORC.topk_f64(s, 40), ORC.topk(s.astype(np.float32), 40))
@@ -472,6 +509,9 @@ MUTANTS = {
     "ascending order": (r"if \(a->score > b->score\) return -1;\n  if \(a->score < b->score\) return 1;",
                         "if (a->score < b->score) return -1;\n  if (a->score > b->score) return 1;"),
     "pad with zero": (r": -1;", ": 0;"),
+    "FP64 selection narrowed to float": (r"c\[b\]\.score = s;", "c[b].score = (float)s;"),
+    "FP64 selection misses a NaN": (r"(const double s = scores\[i \* active_blocks \+ b\];\n\s*)if \(isnan\(s\)\)",
+                                    r"\1if (0)"),
     "signed-zero unequal": (r"c\[b\]\.score = \(double\)s;", "c[b].score = signbit(s) ? -1e-300 : (double)s;"),
     "score via float accumulation": (r"double s = 0\.0;", "float s = 0.0f;"),
     "attention without the scale": (r"s\[c\] = scale \* dot;", "s[c] = dot;"),
