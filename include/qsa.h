@@ -34,7 +34,8 @@
  *         qsa_block_select           under the same condition;
  *         qsa_sparse_decode_attention, qsa_sparse_decode_attention_i8
  *                                    whenever nq >= 1 and heads >= 1.
- *       Never allocate: qsa_block_scores, qsa_block_scores_ex, and
+ *       Never allocate: qsa_block_scores, qsa_block_scores_ex,
+ *         qsa_block_select_noalloc (a static array instead, see there), and
  *         qsa_block_topk / qsa_block_select with nq > QSA_TOPK_FEW_ROWS.
  *     Consequences: make one call of each size on a stream before capturing
  *     that stream into a HIP graph (an allocation during capture fails with
@@ -73,6 +74,7 @@ extern "C" {
 #define QSA_ERR_LAUNCH 5 /* the HIP runtime rejected a launch (hipGetLastError)     */
 #define QSA_ERR_MODE 6   /* unknown precision mode                                  */
 #define QSA_ERR_NOMEM 7  /* the library's device scratch could not be allocated     */
+#define QSA_ERR_SCRATCH 8 /* qsa_block_select_noalloc: the call needs more than its static scratch */
 
 /* Largest heads*dim (elements of one query or one block summary). */
 #define QSA_MAX_HEAD_DIM 4096
@@ -175,6 +177,30 @@ int qsa_block_scores_ex(const float *q, const float *kblk, int nq, int heads, in
  */
 int qsa_block_select(const float *q, const float *kblk, int nq, int heads, int dim,
                      int active_blocks, int k, float *scores, int *ids, void *stream);
+
+/*
+ * qsa_block_select_noalloc -- qsa_block_select for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, checks and results
+ * (bitwise) as qsa_block_select; the caller still passes every input and
+ * output.
+ *
+ * It never calls hipMalloc, hipFree or any allocating routine.  Its scratch
+ * is one static device array of QSA_NOALLOC_SCRATCH_BYTES per GPU, created
+ * with the library's code object and held until the process ends; the first
+ * call on a device looks up the array's address (hipGetSymbolAddress).  That
+ * size covers every call qsa_block_select accepts (at most QSA_TOPK_FEW_ROWS
+ * rows of 16,384 eight-byte words; larger batches need none), and a call
+ * that would need more returns QSA_ERR_SCRATCH before enqueuing anything.
+ *
+ * Every call on one GPU shares that GPU's array, whatever its stream: calls
+ * that overlap on one GPU (on different streams, or from several host
+ * threads without ordering) race and give undefined results.  Calls on one
+ * stream are ordered and safe.  Nothing in the array has to start at zero.
+ */
+#define QSA_NOALLOC_SCRATCH_BYTES 2097152
+int qsa_block_select_noalloc(const float *q, const float *kblk, int nq, int heads, int dim,
+                             int active_blocks, int k, float *scores, int *ids, void *stream);
 
 /*
  * qsa_sparse_decode_attention -- attention of each query over the KV cells of

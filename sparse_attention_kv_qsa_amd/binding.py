@@ -20,6 +20,8 @@ _LIB_NAME = "libqsa.so"
 QSA_OK, QSA_ERR_NULL, QSA_ERR_SHAPE, QSA_ERR_K, QSA_ERR_ALIGN, QSA_ERR_LAUNCH = 0, 1, 2, 3, 4, 5
 QSA_ERR_MODE = 6
 QSA_ERR_NOMEM = 7
+QSA_ERR_SCRATCH = 8
+QSA_NOALLOC_SCRATCH_BYTES = 2097152
 QSA_MAX_HEAD_DIM = 4096
 TOPK_MAX_K = 4096
 MAX_ACTIVE_BLOCKS = 1 << 28
@@ -35,6 +37,7 @@ SIGNATURES = {
     "qsa_block_scores_ex": (_I, [_VP, _VP, _I, _I, _I, _I, _VP, _I, _VP]),
     "qsa_block_topk": (_I, [_VP, _I, _I, _I, _VP, _VP]),
     "qsa_block_select": (_I, [_VP, _VP, _I, _I, _I, _I, _I, _VP, _VP, _VP]),
+    "qsa_block_select_noalloc": (_I, [_VP, _VP, _I, _I, _I, _I, _I, _VP, _VP, _VP]),
     "qsa_sparse_decode_attention": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, ctypes.c_float,
                                          _VP, _VP]),
     "qsa_sparse_decode_attention_i8": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I,
@@ -145,6 +148,20 @@ def qsa_block_select(q: torch.Tensor, kblk: torch.Tensor, k: int, active_blocks:
                      scores: torch.Tensor | None = None, ids: torch.Tensor | None = None):
     """(scores [nq, active_blocks], ids [nq, k]) in one call: the scores of
     qsa_block_scores and the top-k of qsa_block_topk on them."""
+    return _select("qsa_block_select", q, kblk, k, active_blocks, scores, ids)
+
+
+def qsa_block_select_noalloc(q: torch.Tensor, kblk: torch.Tensor, k: int,
+                             active_blocks: int | None = None, scores: torch.Tensor | None = None,
+                             ids: torch.Tensor | None = None):
+    """qsa_block_select with the library's scratch in a static device array
+    instead of an allocation (the library calls no hipMalloc; outputs the
+    caller does not pass are still allocated here, by torch).  Calls that
+    overlap on one GPU race."""
+    return _select("qsa_block_select_noalloc", q, kblk, k, active_blocks, scores, ids)
+
+
+def _select(name, q, kblk, k, active_blocks, scores, ids):
     _require_gpu_f32("q", q, 3)
     _require_gpu_f32("kblk", kblk, 3)
     nq, heads, dim = q.shape
@@ -164,10 +181,10 @@ def qsa_block_select(q: torch.Tensor, kblk: torch.Tensor, k: int, active_blocks:
     elif tuple(ids.shape) != (nq, k) or ids.device != q.device or ids.dtype != torch.int32 or \
             not ids.is_contiguous():
         raise ValueError(f"ids must be a contiguous int32 [{nq}, {k}] tensor on q's device")
-    st = _launch(q.device, load_library().qsa_block_select, q.data_ptr(), kblk.data_ptr(), nq,
+    st = _launch(q.device, getattr(load_library(), name), q.data_ptr(), kblk.data_ptr(), nq,
                  heads, dim, a, k, scores.data_ptr(), ids.data_ptr())
     if st != QSA_OK:
-        raise QSAError(st, "qsa_block_select")
+        raise QSAError(st, name)
     return scores, ids
 
 

@@ -11,6 +11,8 @@
 static_assert(QSA_TOPK_MAX_K == qsa::kTopkMaxK, "header and kernels disagree on the top-k limit");
 static_assert(QSA_ATTN_MAX_DIM == qsa::kAttnMaxDim, "header and kernels disagree on the attention dim");
 static_assert(QSA_TOPK_FEW_ROWS == qsa::kWideMaxRows, "header and kernels disagree on the few-row path");
+static_assert(QSA_NOALLOC_SCRATCH_BYTES == qsa::kNoAllocScratchBytes,
+              "header and kernels disagree on the static scratch size");
 static_assert(QSA_SCORES_AUTO == qsa::kScoresAuto && QSA_SCORES_FP32 == qsa::kScoresFp32 &&
                   QSA_SCORES_BF16X3 == qsa::kScoresBf16x3,
               "header and kernels disagree on the precision modes");
@@ -60,27 +62,64 @@ extern "C" int qsa_block_topk(const float *scores, int nq, int active_blocks, in
                                               static_cast<hipStream_t>(stream)));
 }
 
-extern "C" int qsa_block_select(const float *q, const float *kblk, int nq, int heads, int dim,
-                                int active_blocks, int k, float *scores, int *ids, void *stream) {
+namespace {
+
+// The argument checks of qsa_block_select (and its allocation-free variant).
+// Returns QSA_OK with *done set when the call is a no-op.
+int check_select(const float *q, const float *kblk, int nq, int heads, int dim, int active_blocks,
+                 int k, const float *scores, const int *ids, bool *done) {
+  *done = false;
   if (nq < 0 || heads < 0 || dim < 0 || active_blocks < 0) return QSA_ERR_SHAPE;
   if (active_blocks > QSA_MAX_ACTIVE_BLOCKS) return QSA_ERR_SHAPE;
   const int64_t K = int64_t(heads) * dim;
   if (K < 4 || K % 4 != 0 || K > QSA_MAX_HEAD_DIM) return QSA_ERR_SHAPE;
   if (k < 0 || k > QSA_TOPK_MAX_K) return QSA_ERR_K;
-  if (nq == 0 || (k == 0 && active_blocks == 0)) return QSA_OK;
+  if (nq == 0 || (k == 0 && active_blocks == 0)) {
+    *done = true;
+    return QSA_OK;
+  }
   if (active_blocks > 0 && (!q || !kblk || !scores)) return QSA_ERR_NULL;
   if (k > 0 && !ids) return QSA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(kblk, 16) || !aligned(scores, 4) || !aligned(ids, 4))
     return QSA_ERR_ALIGN;
+  return QSA_OK;
+}
+
+int run_select(const float *q, const float *kblk, int nq, int heads, int dim, int active_blocks,
+               int k, float *scores, int *ids, void *stream, qsa::ScratchFn scratch) {
   (void)hipGetLastError();  // start from a clean launch status
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int K = heads * dim;
   if (k == 0)
     return launch_status(
-        qsa::launch_block_scores(q, kblk, nq, int(K), active_blocks, scores, qsa::kScoresAuto, s));
+        qsa::launch_block_scores(q, kblk, nq, K, active_blocks, scores, qsa::kScoresAuto, s));
   if (active_blocks == 0)
-    return launch_status(qsa::launch_block_topk(scores, nq, 0, k, ids, s));
+    return launch_status(qsa::launch_block_topk(scores, nq, 0, k, ids, s, scratch));
   return launch_status(
-      qsa::launch_block_select(q, kblk, nq, int(K), active_blocks, k, scores, ids, s));
+      qsa::launch_block_select(q, kblk, nq, K, active_blocks, k, scores, ids, s, scratch));
+}
+
+}  // namespace
+
+extern "C" int qsa_block_select(const float *q, const float *kblk, int nq, int heads, int dim,
+                                int active_blocks, int k, float *scores, int *ids, void *stream) {
+  bool done = false;
+  const int st = check_select(q, kblk, nq, heads, dim, active_blocks, k, scores, ids, &done);
+  if (st != QSA_OK || done) return st;
+  return run_select(q, kblk, nq, heads, dim, active_blocks, k, scores, ids, stream,
+                    qsa::workspace);
+}
+
+extern "C" int qsa_block_select_noalloc(const float *q, const float *kblk, int nq, int heads,
+                                        int dim, int active_blocks, int k, float *scores, int *ids,
+                                        void *stream) {
+  bool done = false;
+  const int st = check_select(q, kblk, nq, heads, dim, active_blocks, k, scores, ids, &done);
+  if (st != QSA_OK || done) return st;
+  if (qsa::select_scratch_bytes(nq, heads * dim, active_blocks, k) > QSA_NOALLOC_SCRATCH_BYTES)
+    return QSA_ERR_SCRATCH;
+  return run_select(q, kblk, nq, heads, dim, active_blocks, k, scores, ids, stream,
+                    qsa::static_scratch);
 }
 
 extern "C" int qsa_sparse_decode_attention(const float *q, const float *kcache, const float *vcache,
@@ -142,6 +181,8 @@ extern "C" const char *qsa_strerror(int status) {
       return "unknown precision mode";
     case QSA_ERR_NOMEM:
       return "the library could not allocate its device scratch";
+    case QSA_ERR_SCRATCH:
+      return "the call needs more device scratch than the allocation-free entry point holds";
     default:
       return "unknown status";
   }

@@ -36,14 +36,26 @@ hipError_t launch_block_scores_bf16x3(const float *q, const float *kblk, int nq,
 hipError_t launch_block_scores_fp32(const float *q, const float *kblk, int nq, int K,
                                     int active_blocks, float *scores, hipStream_t stream);
 
-// Device scratch of at least `bytes` bytes for work enqueued on `stream` of
-// the current device (qsa_workspace.hip): one growing buffer per (device,
-// stream), so consecutive calls on one stream reuse it in stream order.
+// The device a stream belongs to (the null stream: the current device).
+hipError_t stream_device(hipStream_t stream, int *dev);
+
+// A source of device scratch: at least `bytes` bytes on the stream's device
+// for work enqueued on `stream`.
+typedef hipError_t (*ScratchFn)(hipStream_t stream, size_t bytes, void **ptr);
+
+// The library's allocating source (qsa_workspace.hip): one growing buffer per
+// (device, stream), so consecutive calls on one stream reuse it in stream
+// order.
 hipError_t workspace(hipStream_t stream, size_t bytes, void **ptr);
+
+// The allocation-free source (qsa_noalloc.hip): one fixed static device array
+// per GPU, shared by every call on that GPU; fails with hipErrorInvalidValue
+// past kNoAllocScratchBytes.
+hipError_t static_scratch(hipStream_t stream, size_t bytes, void **ptr);
 
 // Top-k ids per row of scores[nq][active_blocks]; k in [1, kTopkMaxK].
 hipError_t launch_block_topk(const float *scores, int nq, int active_blocks, int k,
-                             int *ids, hipStream_t stream);
+                             int *ids, hipStream_t stream, ScratchFn scratch = workspace);
 
 // Scores and top-k ids in one call (k >= 1).  For few queries whose scores
 // take the dot-product kernel, the scorer also publishes each 64-block
@@ -51,7 +63,16 @@ hipError_t launch_block_topk(const float *scores, int nq, int active_blocks, int
 // of two; otherwise the two steps run as in separate calls.
 hipError_t launch_block_select(const float *q, const float *kblk, int nq, int K,
                                int active_blocks, int k, float *scores, int *ids,
-                               hipStream_t stream);
+                               hipStream_t stream, ScratchFn scratch = workspace);
+
+// Scratch bytes launch_block_select takes from its source for this call (0
+// when none: many rows, k == 0 or no active block).
+size_t select_scratch_bytes(int nq, int K, int active_blocks, int k);
+
+// The few-row top-k publishes at most this many 8-byte words per row, so a
+// select call needs at most kWideMaxRows * kWideMaxWordsPerRow * 8 bytes.
+constexpr int kWideMaxWordsPerRow = 16384;
+constexpr size_t kNoAllocScratchBytes = size_t(kWideMaxRows) * kWideMaxWordsPerRow * 8;
 
 // Pieces of the fused path.  The whole-GPU top-k groups rows into 64-element
 // groups that publish M rank words each (tops[nq][ngroups][M]).

@@ -582,7 +582,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float *__restrict__ scor
 //   is the same.
 // ---------------------------------------------------------------------------
 constexpr int WIDE_CCAP = 8192;   // LDS candidate capacity
-constexpr int WIDE_UCAP = 16384;  // published words per row, at most
+constexpr int WIDE_UCAP = kWideMaxWordsPerRow;  // published words per row, at most
 constexpr int WIDE_GCAP = WIDE_UCAP / 4;  // groups per row, at most (each publishes >= 4)
 constexpr int WIDE_RCAP = 1024;   // rich groups listed (more: the one-workgroup fallback)
 
@@ -885,12 +885,13 @@ hipError_t launch_rank(const float *scores, int nq, int A, int k, int *ids, cons
 }
 
 template <int E>
-hipError_t launch_wide(const float *scores, int nq, int A, int k, int *ids, hipStream_t stream) {
+hipError_t launch_wide(const float *scores, int nq, int A, int k, int *ids, hipStream_t stream,
+                       ScratchFn scratch) {
   constexpr int GS = 64 * E;
   const int ngroups = (A + GS - 1) / GS;
   const int M = wide_words_per_group(ngroups, k);
   void *ws = nullptr;
-  hipError_t e = workspace(stream, size_t(nq) * ngroups * M * sizeof(uint64_t), &ws);
+  hipError_t e = scratch(stream, size_t(nq) * ngroups * M * sizeof(uint64_t), &ws);
   if (e != hipSuccess) return e;
   uint64_t *tops = static_cast<uint64_t *>(ws);
   group_tops_kernel<E><<<dim3((ngroups + 3) / 4, nq), 256, 0, stream>>>(scores, A, ngroups, M, tops);
@@ -921,15 +922,35 @@ hipError_t launch_wide_rank(const float *scores, int nq, int A, int k, int *ids,
   return launch_rank<1>(scores, nq, A, k, ids, tops, ngroups, M, stream);
 }
 
+// Elements per group of the few-row top-k for a row of A scores (0: the row
+// takes the one-workgroup path).  The group size grows with the row so that
+// the published words stay within WIDE_UCAP (ngroups <= WIDE_UCAP / 4: every
+// group publishes at least 4 words).
+int wide_group_size(int nq, int A) {
+  if (nq > kWideMaxRows || A <= 0 || A > 2048 * 1024) return 0;
+  return A <= 2048 * 64 ? 64 : A <= 2048 * 256 ? 256 : 1024;
+}
+
+size_t select_scratch_bytes(int nq, int K, int A, int k) {
+  if (nq <= 0 || A <= 0 || k <= 0) return 0;
+  if (nq <= kWideMaxRows && A <= kWideMaxBlocksFused && gemv_fits(nq, K)) {
+    const int ngroups = (A + 63) / 64;
+    return size_t(nq) * ngroups * wide_words_per_group(ngroups, k) * sizeof(uint64_t);
+  }
+  const int gs = wide_group_size(nq, A);
+  if (gs == 0) return 0;
+  const int ngroups = (A + gs - 1) / gs;
+  return size_t(nq) * ngroups * wide_words_per_group(ngroups, k) * sizeof(uint64_t);
+}
+
 hipError_t launch_block_topk(const float *scores, int nq, int A, int k, int *ids,
-                             hipStream_t stream) {
-  // Few rows: spread each row over the GPU (group size grows with the row so
-  // that the published words stay within WIDE_UCAP).
-  // (ngroups <= WIDE_UCAP / 4: every group publishes at least 4 words.)
-  if (nq <= kWideMaxRows && A > 0 && A <= 2048 * 1024) {
-    if (A <= 2048 * 64) return launch_wide<1>(scores, nq, A, k, ids, stream);
-    if (A <= 2048 * 256) return launch_wide<4>(scores, nq, A, k, ids, stream);
-    return launch_wide<16>(scores, nq, A, k, ids, stream);
+                             hipStream_t stream, ScratchFn scratch) {
+  // Few rows: spread each row over the GPU.
+  switch (wide_group_size(nq, A)) {
+    case 64: return launch_wide<1>(scores, nq, A, k, ids, stream, scratch);
+    case 256: return launch_wide<4>(scores, nq, A, k, ids, stream, scratch);
+    case 1024: return launch_wide<16>(scores, nq, A, k, ids, stream, scratch);
+    default: break;
   }
   // Register width from the active block count only: the smallest PER with
   // (PER + 1) * NT >= A; longer rows stream from memory on every pass.

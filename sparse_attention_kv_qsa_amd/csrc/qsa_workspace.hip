@@ -38,8 +38,7 @@ std::vector<void *> g_retired;  // outgrown buffers, kept for the process lifeti
 
 }  // namespace
 
-// The device a stream belongs to (the null stream: the current device).
-static hipError_t stream_device(hipStream_t stream, int *dev) {
+hipError_t stream_device(hipStream_t stream, int *dev) {
   if (stream == nullptr) return hipGetDevice(dev);
   hipDevice_t d = 0;
   const hipError_t e = hipStreamGetDevice(stream, &d);

@@ -34,6 +34,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert header_entry_points() == ["qsa_block_scores", "qsa_block_scores_ex", "qsa_block_select",
+                                     "qsa_block_select_noalloc",
                                      "qsa_block_topk", "qsa_sparse_decode_attention",
                                      "qsa_sparse_decode_attention_i8", "qsa_strerror"]
 
@@ -50,6 +51,8 @@ def test_binding_covers_the_header():
     assert mac["QSA_TOPK_FEW_ROWS"] == binding.TOPK_FEW_ROWS
     assert mac["QSA_ERR_MODE"] == binding.QSA_ERR_MODE
     assert mac["QSA_ERR_NOMEM"] == binding.QSA_ERR_NOMEM
+    assert mac["QSA_ERR_SCRATCH"] == binding.QSA_ERR_SCRATCH
+    assert mac["QSA_NOALLOC_SCRATCH_BYTES"] == binding.QSA_NOALLOC_SCRATCH_BYTES
     assert (mac["QSA_SCORES_AUTO"], mac["QSA_SCORES_FP32"], mac["QSA_SCORES_BF16X3"]) == (
         binding.QSA_SCORES_AUTO, binding.QSA_SCORES_FP32, binding.QSA_SCORES_BF16X3)
     assert mac["QSA_MAX_HEAD_DIM"] == binding.QSA_MAX_HEAD_DIM
@@ -73,8 +76,8 @@ def test_library_is_built_for_gfx950_only():
 
 
 def test_strerror(lib):
-    for code in range(8):
-        assert binding.qsa_strerror(code)
+    for code in range(9):
+        assert binding.qsa_strerror(code) != "unknown status"
     assert binding.qsa_strerror(0) == "success"
     assert binding.qsa_strerror(99) == "unknown status"
 
@@ -145,8 +148,9 @@ def test_block_topk_argument_checks(lib, args, status):
     ((None, None, 0, 4, 128, 10, 4, None, None), binding.QSA_OK),   # nq = 0: no-op
     ((None, None, 2, 4, 128, 0, 0, None, None), binding.QSA_OK),    # nothing to do
 ])
-def test_block_select_argument_checks(lib, args, status):
-    assert lib.qsa_block_select(*args, None) == status
+@pytest.mark.parametrize("entry", ["qsa_block_select", "qsa_block_select_noalloc"])
+def test_block_select_argument_checks(lib, entry, args, status):
+    assert getattr(lib, entry)(*args, None) == status
 
 
 @pytest.mark.parametrize("args,status", [
