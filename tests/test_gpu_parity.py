@@ -129,6 +129,8 @@ RAND_CASES = [  # nq, heads, dim, active
     (1, 16, 256, 300), (2, 8, 256, 200), (4, 4, 256, 100), (8, 2, 256, 50),
     (9, 4, 128, 1025), (33, 4, 64, 2000), (64, 4, 128, 4096), (256, 4, 128, 2113),
     (200, 4, 100, 515), (16, 32, 128, 70), (40, 1, 4, 333), (12, 3, 20, 64),
+    # wide ragged columns (33..63 blocks) with LDS-staged query rows
+    (130, 4, 128, 1000), (150, 4, 64, 2047),
 ]
 
 
