@@ -289,3 +289,39 @@ def test_decode_layer_replays_from_a_graph(nq, active, k):
         torch.cuda.synchronize()
     # the eager outputs are still the expected ones after the replays
     check_attn(q, kc, vc, want[1].cpu().numpy(), 4 * active, 1.0 / np.sqrt(dim))
+
+
+def test_decode_layers_on_concurrent_streams():
+    """Three decode layers (select, then attention over the selected cells)
+    enqueued interleaved on three streams, with no synchronisation between
+    them: each stream has its own library scratch, so every stream's results
+    equal those of the same layer run alone on the default stream."""
+    from sparse_attention_kv_qsa_amd import qsa_block_select, qsa_sparse_decode_attention
+    rng = np.random.default_rng(77)
+    layers = []
+    for nq, active, k in [(1, 32770, 512), (2, 20000, 300), (4, 9000, 1024)]:
+        q = torch.from_numpy(rng.standard_normal((nq, 4, 128)).astype(np.float32)).cuda()
+        kb = torch.from_numpy(rng.standard_normal((active, 4, 128)).astype(np.float32)).cuda()
+        kc = torch.from_numpy(rng.standard_normal((4 * active, 4, 128)).astype(np.float32)).cuda()
+        vc = torch.from_numpy(rng.standard_normal((4 * active, 4, 128)).astype(np.float32)).cuda()
+        layers.append((q, kb, kc, vc, active, k))
+
+    def run(layer):
+        q, kb, kc, vc, active, k = layer
+        s, ids = qsa_block_select(q, kb, k, active)
+        return s, ids, qsa_sparse_decode_attention(q, kc, vc, ids, 4 * active)
+
+    refs = [run(layer) for layer in layers]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in layers]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    results = [None] * len(layers)
+    for rep in range(3):
+        for i, (st, layer) in enumerate(zip(streams, layers)):
+            with torch.cuda.stream(st):
+                results[i] = run(layer)
+    torch.cuda.synchronize()
+    for got, want in zip(results, refs):
+        for a, b in zip(got, want):
+            assert torch.equal(a, b)

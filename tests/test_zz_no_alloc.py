@@ -85,3 +85,38 @@ def test_noalloc_edges(lib):
     s_ref, _ = c_select(lib, "qsa_block_select", q, kb, 100, 0)
     torch.cuda.synchronize()
     assert torch.equal(s, s_ref)
+
+
+def test_noalloc_first_call_captured_in_a_graph(lib):
+    """The allocation-free select needs no warm-up call before capture: the
+    first call on a fresh stream goes straight into a HIP graph.  Three
+    replays, with eager library work and synchronisations between them, each
+    reproduce the eager results bitwise."""
+    from sparse_attention_kv_qsa_amd import qsa_block_select, qsa_block_select_noalloc
+    shapes = [(1, 4, 128, 32770, 512), (2, 4, 64, 300000, 256)]  # fused decode; scorer + groups of 256
+    ins, outs, refs = [], [], []
+    for n, (nq, heads, dim, active, k) in enumerate(shapes):
+        q, kb = inputs(nq, heads, dim, active, seed=40 + n)
+        ins.append((q, kb, active, k))
+        outs.append((torch.empty((nq, active), dtype=torch.float32, device="cuda"),
+                     torch.empty((nq, k), dtype=torch.int32, device="cuda")))
+        refs.append(qsa_block_select(q, kb, k, active))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for (q, kb, active, k), (s, ids) in zip(ins, outs):
+            qsa_block_select_noalloc(q, kb, k, active, scores=s, ids=ids)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for s, ids in outs:
+            s.fill_(-3.0)
+            ids.fill_(-9)
+        q, kb, active, k = ins[1]
+        qsa_block_select_noalloc(q, kb, 17, 5000)   # eager work sharing the static scratch
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (s, ids), (s_ref, ids_ref) in zip(outs, refs):
+            assert torch.equal(s, s_ref) and torch.equal(ids, ids_ref), f"replay {rep}"
