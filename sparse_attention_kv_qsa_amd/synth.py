@@ -69,7 +69,8 @@ class Workload:
 # call inside a 262,144-cell capacity, and a 256K near-tie prompt stress case;
 # then multi-query decode at 128K (2 and 4 queries per call, the T = 2 and
 # T = 4 rows of the decode table of "#3108 perf(hip): ...": speculative
-# verification scores several queries against the same summaries).
+# verification scores several queries against the same summaries), and one
+# eighth of the 128K prompt's blocks (the share of one of 8 GPUs).
 WORKLOADS = {
     w.name: w
     for w in [
@@ -86,6 +87,10 @@ WORKLOADS = {
                  k=512, poison=True),
         Workload("decode-128k-t4", nq=4, heads=4, dim=128, active=32770, capacity=65538,
                  k=512, poison=True),
+        # One GPU's share of the 128K prompt when the blocks are split over 8
+        # GPUs by range: the per-shard call at its real shape.
+        Workload("prompt-128k-shard8", nq=256, heads=4, dim=128, active=4097, capacity=4097,
+                 k=512, needle_frac=0.01),
     ]
 }
 

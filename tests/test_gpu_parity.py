@@ -446,3 +446,48 @@ def test_workload_parity(name, mode):
         for b, j in zip(bt.needle_blocks[:50], bt.needle_queries[:50]):
             sel.add(int(b) in set(ids[j].tolist()))
         assert sel == {True}
+
+
+# ------------------------------------------------ sharding, on one GPU ----
+
+@pytest.mark.parametrize("nq,active,k,ties", [(256, 32770, 512, 0), (1, 32770, 512, 0),
+                                               (64, 20000, 300, 7), (3, 5000, 1024, 0)])
+def test_sharded_select_merges_exactly(nq, active, k, ties):
+    """The block-range sharding of the selection: G = 8 shards each select
+    their own top k over their block range (ids local to the shard); the
+    shards' winners, concatenated in shard order, are selected again.  A
+    block's score does not depend on which call or tile holds it, and equal
+    scores resolve by concatenation index, which is the global id order
+    (shards in range order, each list in rank order), so the merged selection
+    equals the one-call selection id for id."""
+    from sparse_attention_kv_qsa_amd import qsa_block_select, qsa_block_topk
+    G = 8
+    rng = np.random.default_rng(active + nq)
+    q = rng.standard_normal((nq, 4, 128)).astype(np.float32)
+    if ties:
+        vec = rng.standard_normal((ties, 4, 128)).astype(np.float32)
+        kb = np.ascontiguousarray(vec[rng.integers(0, ties, active)])
+    else:
+        kb = rng.standard_normal((active, 4, 128)).astype(np.float32)
+    qt, kt = torch.from_numpy(q).cuda(), torch.from_numpy(kb).cuda()
+    s_all, ids_all = qsa_block_select(qt, kt, k, active)
+    bounds = [active * g // G for g in range(G + 1)]
+    cand_s, cand_id, shard_s = [], [], []
+    for g in range(G):
+        lo, hi = bounds[g], bounds[g + 1]
+        s_g, ids_g = qsa_block_select(qt, kt[lo:hi].contiguous(), k, hi - lo)
+        shard_s.append(s_g)
+        ok = ids_g >= 0
+        sel = torch.gather(s_g, 1, ids_g.clamp(min=0).long())
+        # padding slots (k > shard size) take -inf and an id past every block
+        cand_s.append(torch.where(ok, sel, torch.full_like(sel, -float("inf"))))
+        cand_id.append(torch.where(ok, ids_g + lo, torch.full_like(ids_g, 2 ** 30)))
+    cs = torch.cat(cand_s, dim=1).contiguous()
+    ci = torch.cat(cand_id, dim=1)
+    pick = qsa_block_topk(cs, k)
+    merged = torch.gather(ci, 1, pick.clamp(min=0).long())
+    merged = torch.where(pick >= 0, merged, torch.full_like(merged, -1))
+    torch.cuda.synchronize()
+    assert torch.equal(merged.int(), ids_all)
+    # and the shards' scores are the one call's scores, bit for bit
+    assert torch.equal(torch.cat(shard_s, dim=1), s_all)

@@ -11,13 +11,17 @@ def test_workload_table():
     w = synth.WORKLOADS
     assert [x.name for x in w.values()] == ["tiny-decode", "prompt-32k", "decode-128k",
                                             "prompt-128k", "prompt-256k-tie",
-                                            "decode-128k-t2", "decode-128k-t4"]
+                                            "decode-128k-t2", "decode-128k-t4",
+                                            "prompt-128k-shard8"]
     assert [w[n].nq for n in ("decode-128k", "decode-128k-t2", "decode-128k-t4")] == [1, 2, 4]
     assert (w["tiny-decode"].active, w["tiny-decode"].K, w["tiny-decode"].k) == (512, 256, 64)
     assert (w["prompt-32k"].nq, w["prompt-32k"].active, w["prompt-32k"].k) == (256, 8193, 256)
     assert (w["decode-128k"].active, w["decode-128k"].capacity) == (32770, 65538)
     assert (w["prompt-128k"].n_needles, w["prompt-32k"].n_needles) == (328, 82)
     assert w["prompt-256k-tie"].n_needles == 66
+    # one of 8 GPUs' share of the 128K prompt's blocks (ranges of 4,096 or 4,097)
+    sh = w["prompt-128k-shard8"]
+    assert (sh.nq, sh.active, sh.k) == (256, -(-w["prompt-128k"].active // 8), 512)
     # a 262,144-cell capacity is max-context/4 + 2 blocks
     assert w["prompt-128k"].capacity == 262144 // 4 + 2
 
