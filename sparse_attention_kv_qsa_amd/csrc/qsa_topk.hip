@@ -26,8 +26,12 @@
 //      block id (lowest first) among keys == T, so ties go to the lower block
 //      id.  (If the candidates overflow LDS, the passes run over the
 //      register-resident row instead; the result is the same.)
-//   4. bitonic sort into rank order (key desc, id asc): in registers with lane
-//      exchanges for strides < 64, through LDS above that.
+//   4. rank order (key desc, id asc).  Up to NT pairs: a counting rank --
+//      buckets by key, one prefix sum over the bucket counts, then a count of
+//      the larger words inside each pair's own bucket -- unless a bucket
+//      takes more than kBucketCap pairs (bulk ties); then, and beyond NT
+//      pairs, a bitonic sort: in registers with lane exchanges for strides
+//      < 64, through LDS above that.
 #include <hip/hip_runtime.h>
 
 #include "qsa_device.h"
@@ -48,7 +52,9 @@ struct TopkShared {
   uint32_t bcast[3];           // chosen digit, remaining k, count in the bin
   uint32_t ncand;              // candidates gathered
   uint32_t nwin;               // winners gathered
-  uint32_t wmin[NWAVES];       // per-wave candidate bound
+  uint32_t wmin[NWAVES];       // per-wave candidate bound; per-wave smallest key of the counting rank
+  uint32_t wmax[NWAVES];       // per-wave largest key of the counting rank
+  uint32_t big;                // the counting rank met a bucket past its cap
   union {
     struct {
       uint32_t ckey[CAP];      // candidates: keys ...
@@ -107,6 +113,7 @@ __device__ __forceinline__ void find_digit(TopkShared &sh, uint32_t sub0, uint32
 struct Threshold {
   uint32_t pref = 0, mask = 0;
   uint32_t idpref = 0, idmask = 0, idtop = 0;
+  uint32_t tied = 0;  // winners that share the whole key T (pref, with a full mask)
   bool by_id = false;
   __device__ bool wins(uint32_t id, uint32_t key) const {
     const uint32_t kp = key & mask;
@@ -150,10 +157,14 @@ __device__ __forceinline__ Threshold radix_select(TopkShared &sh, Visit &&visit,
     find_digit(sh, th.pref == 0 ? n_sentinel : 0u, kr, d, cnt);
     th.pref |= d << shift;
     th.mask |= 0xFFu << shift;
-    if (cnt == kr) return th;
+    if (cnt == kr) {
+      if (shift == 0) th.tied = kr;
+      return th;
+    }
   }
   // More keys equal T = pref than are still needed: take the kr lowest ids.
   th.by_id = true;
+  th.tied = kr;
   const int idbits = 32 - __clz(uint32_t(A - 1));
   th.idtop = idbits >= 32 ? 0xFFFFFFFFu : ((1u << idbits) - 1u);
   for (int shift = 8 * ((idbits + 7) / 8 - 1); shift >= 0; shift -= 8) {
@@ -292,17 +303,118 @@ __device__ __forceinline__ void sort_wide(const uint32_t *skey, const uint32_t *
   for (int r = m + t; r < k; r += NT) orow[r] = -1;
 }
 
+// Exclusive prefix sum of v over the workgroup (NT threads) and the total.
+// One barrier; `wsum` is NWAVES words of scratch.  Every thread must call it.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wsum, uint32_t &total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  const uint32_t ws = wave_incl_scan(lane < NWAVES ? wsum[lane] : 0u);
+  total = __builtin_amdgcn_readlane(ws, NWAVES - 1);
+  const uint32_t before = wave > 0 ? __builtin_amdgcn_readlane(ws, wave - 1) : 0u;
+  return before + incl - v;
+}
+
+// Buckets of the counting rank, and the most pairs it lets one bucket take.
+constexpr int kRankBuckets = NT;
+constexpr uint32_t kBucketCap = 64;
+
+// Rank-order store of n <= NT (key, id) pairs (skey/sid in LDS) by counting
+// instead of a sorting network: each pair goes to one of NT buckets by key
+// (equal ranges of key values from the largest key down to the smallest, so
+// every key of bucket b is larger than every key of bucket b + 1), one prefix
+// sum over the bucket counts gives each bucket's first rank, and a pair's
+// rank is that plus the number of larger rank words in its own bucket.  The
+// pair of rank r < m stores its id at orow[r]; orow[m, k) gets -1.  Returns
+// false, having stored nothing, when a bucket receives more than kBucketCap
+// pairs (ties or near-ties in bulk): the caller then sorts with the network.
+// Five barriers; every thread of the workgroup must call it.
+__device__ __forceinline__ bool counting_rank_store(const uint32_t *skey, const uint32_t *sid, int n,
+                                                    int m, int k, int *__restrict__ orow,
+                                                    TopkShared &sh) {
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const bool live = t < n;
+  const uint32_t key = live ? skey[t] : 0u;
+  const uint32_t id = live ? sid[t] : 0u;
+  uint32_t hi = key, lo = live ? key : 0xFFFFFFFFu;
+  hi = max(hi, lane_xor<1>(hi)); lo = min(lo, lane_xor<1>(lo));
+  hi = max(hi, lane_xor<2>(hi)); lo = min(lo, lane_xor<2>(lo));
+  hi = max(hi, lane_xor<4>(hi)); lo = min(lo, lane_xor<4>(lo));
+  hi = max(hi, lane_xor<8>(hi)); lo = min(lo, lane_xor<8>(lo));
+  hi = max(hi, lane_xor<16>(hi)); lo = min(lo, lane_xor<16>(lo));
+  hi = max(hi, lane_xor<32>(hi)); lo = min(lo, lane_xor<32>(lo));
+  uint32_t *cnt = &sh.hsub[0][0];  // bucket counts, then each bucket's first rank
+  uint32_t *wsum = cnt + kRankBuckets;
+  if (lane == 0) {
+    sh.wmin[wave] = lo;
+    sh.wmax[wave] = hi;
+  }
+  cnt[t] = 0u;
+  if (t == 0) sh.big = 0u;
+  __syncthreads();
+  hi = 0u;
+  lo = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < NWAVES; ++w) {
+    hi = max(hi, sh.wmax[w]);
+    lo = min(lo, sh.wmin[w]);
+  }
+  // Bucket of a key: (hi - key) >> shift, below kRankBuckets for every key in [lo, hi].
+  const uint32_t span = hi - lo;
+  const int shift = max(0, 32 - __builtin_clz(span | 1u) - 10);
+  const uint32_t b = (hi - key) >> shift;
+  uint32_t within = 0;
+  if (live) {
+    within = atomicAdd(&cnt[b], 1u);
+    if (within >= kBucketCap) sh.big = 1u;
+  }
+  __syncthreads();
+  if (sh.big) return false;
+  uint32_t total;
+  const uint32_t first = block_excl_scan(cnt[t], wsum, total);
+  cnt[t] = first;
+  uint64_t *sw = sh.wbuf;
+  if (t < 4) sw[n + t] = 0ull;  // the rank loop reads up to three words past the last bucket
+  __syncthreads();
+  const uint64_t word = rank_word(key, id);
+  uint32_t start = 0, end = 0;
+  if (live) {
+    start = cnt[b];
+    end = b + 1 < uint32_t(kRankBuckets) ? cnt[b + 1] : uint32_t(n);
+    sw[start + within] = word;
+  }
+  __syncthreads();
+  if (live) {
+    // Words past the bucket's end belong to later buckets (smaller keys) or
+    // are the zero padding: comparing with them adds nothing.
+    uint32_t r = start;
+    for (uint32_t j = start; j < end; j += 4)
+      r += uint32_t(sw[j] > word) + uint32_t(sw[j + 1] > word) + uint32_t(sw[j + 2] > word) +
+           uint32_t(sw[j + 3] > word);
+    if (r < uint32_t(m)) orow[r] = int(id);
+  }
+  for (int r = m + t; r < k; r += NT) orow[r] = -1;
+  return true;
+}
+
 // Rank-order sort of the n (key, id) pairs in LDS arrays skey/sid, then the
 // store of one row of ids: the first m in rank order, then -1 up to k.
 // `wbuf` is 2 NT words of LDS scratch; `xbuf`, 2 MAXK words, is used only
 // for n > NT and must not overlap skey/sid.  Every thread of the workgroup
 // must call it.
 __device__ __forceinline__ void sort_and_store(uint32_t *skey, uint32_t *sid, int n, int m, int k,
-                               int *__restrict__ orow, uint64_t *wbuf, uint64_t *xbuf) {
+                               int *__restrict__ orow, TopkShared &sh, uint64_t *xbuf,
+                               bool try_count = true) {
   const int t = threadIdx.x;
+  uint64_t *wbuf = sh.wbuf;
   int P = 1;
   while (P < n) P <<= 1;
   if (P <= NT) {
+    if (try_count && counting_rank_store(skey, sid, n, m, k, orow, sh)) return;
     // One rank word per thread (padding: word 0, after every element).
     // Strides below 64 exchange inside the wave, larger strides through LDS.
     // Waves past the P elements only keep the barriers.
@@ -518,9 +630,10 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
   if (C <= uint32_t(NT)) {
     // Few candidates (the usual case): sort them all into rank order and
     // keep the first m -- every winner is a candidate.
-    sort_and_store(sh.cu.c.ckey, sh.cu.c.cid, int(C), m, k, orow, sh.wbuf, nullptr);
+    sort_and_store(sh.cu.c.ckey, sh.cu.c.cid, int(C), m, k, orow, sh, nullptr);
     return;
   }
+  bool try_count = true;
   if (C <= uint32_t(CAP)) {
     // Select among the LDS candidates (all of them when k >= C).
     const uint32_t padC = (C + NT - 1) / NT * NT;
@@ -534,14 +647,20 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
     if (uint32_t(k) < C) th = radix_select(sh, visit_cand, uint32_t(k), padC - C, A);
     compact(visit_cand, [&](uint32_t id, uint32_t key) { return key != 0u && th.wins(id, key); },
             &sh.nwin, sh.bkey, sh.bid, MAXK);
+    try_count = !th.by_id && th.tied <= kBucketCap;
   } else {
     // Too many candidates for LDS: select over the whole row.
     const Threshold th = radix_select(sh, visit_row, uint32_t(k), n_sentinel, A);
     compact(visit_row, [&](uint32_t id, uint32_t key) { return key != 0u && th.wins(id, key); },
             &sh.nwin, sh.bkey, sh.bid, MAXK);
+    try_count = !th.by_id && th.tied <= kBucketCap;
   }
   __syncthreads();
-  sort_and_store(sh.bkey, sh.bid, m, m, k, orow, sh.wbuf, sh.cu.xbuf);
+  // A select that had to split the keys equal to its threshold by id met
+  // ties in bulk, and winners that share one key share one bucket of the
+  // counting rank: past its cap, go straight to the network (a failed
+  // attempt costs about a microsecond on rows of thousand-way ties).
+  sort_and_store(sh.bkey, sh.bid, m, m, k, orow, sh, sh.cu.xbuf, try_count);
 }
 
 template <int PER>
@@ -676,19 +795,6 @@ union WideLds {
   TopkShared row;
 };
 
-// Exclusive prefix sum of v over the workgroup (NT threads) and the total.
-// One barrier; `wsum` is NWAVES words of scratch.  Every thread must call it.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wsum, uint32_t &total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_incl_scan(v);
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  const uint32_t ws = wave_incl_scan(lane < NWAVES ? wsum[lane] : 0u);
-  total = __builtin_amdgcn_readlane(ws, NWAVES - 1);
-  const uint32_t before = wave > 0 ? __builtin_amdgcn_readlane(ws, wave - 1) : 0u;
-  return before + incl - v;
-}
 
 template <int E, int WPT>
 __global__ __launch_bounds__(NT) void wide_rank_kernel(const float *__restrict__ scores, int A,

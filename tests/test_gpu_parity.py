@@ -301,6 +301,38 @@ def test_topk_special_rows(path):
     assert ids.tolist() == list(range(10)), "-0.0 and +0.0 must tie (lower id first)"
 
 
+def counting_rank_rows(rng, a):
+    """Rows aimed at the one-workgroup top-k's counting rank (rank order of up
+    to 1,024 pairs from 1,024 buckets of equal key ranges, a bucket capped at
+    64 pairs, the sorting network past the cap): keys evenly spaced so that
+    each bucket holds one, then one value repeated to fill its bucket exactly
+    to the cap and one past it; a thousand consecutive floats (near-ties in
+    one bucket) among random scores; and the widest key span, -Inf to +Inf."""
+    even = (np.uint32(0x3F800000) + np.arange(a, dtype=np.uint32) * np.uint32(4096)).view(np.float32)
+    rows = []
+    for extra in (63, 64):  # the largest value's bucket: 64 pairs, then 65
+        r = even.copy()
+        r[rng.choice(a - 1, extra, replace=False)] = even[a - 1]
+        rows.append(r)
+    r = (rng.standard_normal(a) * 20).astype(np.float32)
+    near = (np.float32(30.0).view(np.uint32) + np.arange(min(a, 1000), dtype=np.uint32)).view(np.float32)
+    r[rng.choice(a, len(near), replace=False)] = near
+    rows.append(r)
+    r = rng.standard_normal(a).astype(np.float32)
+    r[:4] = [np.inf, -np.inf, np.finfo(np.float32).max, -np.finfo(np.float32).max]
+    rows.append(r)
+    return np.ascontiguousarray(np.stack(rows).astype(np.float32))
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("a,k", [(1000, 1000), (1000, 300), (1024, 1024), (1025, 1025),
+                                  (4097, 512), (32770, 512), (65538, 1024)])
+def test_topk_counting_rank(a, k, path):
+    s = counting_rank_rows(np.random.default_rng(a * 5 + k), a)
+    ids = check_topk(s, k, path)
+    assert topk_invariants(rows_for_path(s, path), ids, k) == []
+
+
 def test_topk_deterministic():
     rng = np.random.default_rng(5)
     s = tie_rows(rng, 8, 40000, 50)
