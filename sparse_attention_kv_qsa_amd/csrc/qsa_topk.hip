@@ -317,6 +317,11 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wsum, 
   return before + incl - v;
 }
 
+// Keys known to lie in [lo, hi].
+struct KeyRange {
+  uint32_t lo, hi;
+};
+
 // Buckets of the counting rank, and the most pairs it lets one bucket take.
 constexpr int kRankBuckets = NT;
 constexpr uint32_t kBucketCap = 64;
@@ -333,35 +338,44 @@ constexpr uint32_t kBucketCap = 64;
 // Five barriers; every thread of the workgroup must call it.
 __device__ __forceinline__ bool counting_rank_store(const uint32_t *skey, const uint32_t *sid, int n,
                                                     int m, int k, int *__restrict__ orow,
-                                                    TopkShared &sh) {
+                                                    TopkShared &sh, bool known, KeyRange range) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
   const bool live = t < n;
   const uint32_t key = live ? skey[t] : 0u;
   const uint32_t id = live ? sid[t] : 0u;
-  uint32_t hi = key, lo = live ? key : 0xFFFFFFFFu;
-  hi = max(hi, lane_xor<1>(hi)); lo = min(lo, lane_xor<1>(lo));
-  hi = max(hi, lane_xor<2>(hi)); lo = min(lo, lane_xor<2>(lo));
-  hi = max(hi, lane_xor<4>(hi)); lo = min(lo, lane_xor<4>(lo));
-  hi = max(hi, lane_xor<8>(hi)); lo = min(lo, lane_xor<8>(lo));
-  hi = max(hi, lane_xor<16>(hi)); lo = min(lo, lane_xor<16>(lo));
-  hi = max(hi, lane_xor<32>(hi)); lo = min(lo, lane_xor<32>(lo));
   uint32_t *cnt = &sh.hsub[0][0];  // bucket counts, then each bucket's first rank
   uint32_t *wsum = cnt + kRankBuckets;
-  if (lane == 0) {
-    sh.wmin[wave] = lo;
-    sh.wmax[wave] = hi;
-  }
-  cnt[t] = 0u;
-  if (t == 0) sh.big = 0u;
-  __syncthreads();
-  hi = 0u;
-  lo = 0xFFFFFFFFu;
+  uint32_t hi, lo;
+  if (known) {
+    // The candidates of one row: keys in [bound, row maximum]; the counts
+    // and the flag were cleared when the row started.
+    lo = range.lo;
+    hi = range.hi;
+  } else {
+    hi = key;
+    lo = live ? key : 0xFFFFFFFFu;
+    hi = max(hi, lane_xor<1>(hi)); lo = min(lo, lane_xor<1>(lo));
+    hi = max(hi, lane_xor<2>(hi)); lo = min(lo, lane_xor<2>(lo));
+    hi = max(hi, lane_xor<4>(hi)); lo = min(lo, lane_xor<4>(lo));
+    hi = max(hi, lane_xor<8>(hi)); lo = min(lo, lane_xor<8>(lo));
+    hi = max(hi, lane_xor<16>(hi)); lo = min(lo, lane_xor<16>(lo));
+    hi = max(hi, lane_xor<32>(hi)); lo = min(lo, lane_xor<32>(lo));
+    if (lane == 0) {
+      sh.wmin[wave] = lo;
+      sh.wmax[wave] = hi;
+    }
+    cnt[t] = 0u;
+    if (t == 0) sh.big = 0u;
+    __syncthreads();
+    hi = 0u;
+    lo = 0xFFFFFFFFu;
 #pragma unroll
-  for (int w = 0; w < NWAVES; ++w) {
-    hi = max(hi, sh.wmax[w]);
-    lo = min(lo, sh.wmin[w]);
+    for (int w = 0; w < NWAVES; ++w) {
+      hi = max(hi, sh.wmax[w]);
+      lo = min(lo, sh.wmin[w]);
+    }
   }
   // Bucket of a key: (hi - key) >> shift, below kRankBuckets for every key in [lo, hi].
   const uint32_t span = hi - lo;
@@ -408,13 +422,14 @@ __device__ __forceinline__ bool counting_rank_store(const uint32_t *skey, const 
 // must call it.
 __device__ __forceinline__ void sort_and_store(uint32_t *skey, uint32_t *sid, int n, int m, int k,
                                int *__restrict__ orow, TopkShared &sh, uint64_t *xbuf,
-                               bool try_count = true) {
+                               bool try_count = true, bool known = false,
+                               KeyRange range = KeyRange{0u, 0u}) {
   const int t = threadIdx.x;
   uint64_t *wbuf = sh.wbuf;
   int P = 1;
   while (P < n) P <<= 1;
   if (P <= NT) {
-    if (try_count && counting_rank_store(skey, sid, n, m, k, orow, sh)) return;
+    if (try_count && counting_rank_store(skey, sid, n, m, k, orow, sh, known, range)) return;
     // One rank word per thread (padding: word 0, after every element).
     // Strides below 64 exchange inside the wave, larger strides through LDS.
     // Waves past the P elements only keep the barriers.
@@ -500,6 +515,7 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
   if (t == 0) {
     sh.ncand = 0;
     sh.nwin = 0;
+    sh.big = 0;
   }
 
   // Raw buffer loads: the hardware returns 0 past the row end, so every
@@ -569,6 +585,8 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
   // it and one row in ten overflowed the direct sort; with two, about 2 %.)
   // Beyond k = 4 NT the bound is 1: every real key is a candidate.
   uint32_t bound = 1u;
+  KeyRange range{0u, 0u};  // the candidates' keys, set with the bound
+  bool ranged = false;
   if (k < A && k <= 4 * NT) {
     // Up to k = NT each thread keeps its two largest keys, beyond that its
     // four (kw <= 64 or 256 values of the wave are then enough).
@@ -614,12 +632,30 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
       if (four) n += uint32_t(__popcll(__ballot(v2 >= c))) + uint32_t(__popcll(__ballot(v3 >= c)));
       if (n >= uint32_t(kw)) vw = c;
     }
-    if (lane == 0) sh.wmin[wave] = vw;
+    // The row's largest key (each thread's largest is v0).
+    uint32_t mx = v0;
+    mx = max(mx, lane_xor<1>(mx));
+    mx = max(mx, lane_xor<2>(mx));
+    mx = max(mx, lane_xor<4>(mx));
+    mx = max(mx, lane_xor<8>(mx));
+    mx = max(mx, lane_xor<16>(mx));
+    mx = max(mx, lane_xor<32>(mx));
+    if (lane == 0) {
+      sh.wmin[wave] = vw;
+      sh.wmax[wave] = mx;
+    }
     __syncthreads();
     uint32_t b = 0xFFFFFFFFu;
+    mx = 0u;
 #pragma unroll
-    for (int w = 0; w < NWAVES; ++w) b = min(b, sh.wmin[w]);
+    for (int w = 0; w < NWAVES; ++w) {
+      b = min(b, sh.wmin[w]);
+      mx = max(mx, sh.wmax[w]);
+    }
     bound = max(b, 1u);
+    range.lo = bound;
+    range.hi = max(mx, bound);
+    ranged = true;
   }
 
   compact(visit_row, [&](uint32_t, uint32_t key) { return key >= bound; }, &sh.ncand, sh.cu.c.ckey,
@@ -630,7 +666,8 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
   if (C <= uint32_t(NT)) {
     // Few candidates (the usual case): sort them all into rank order and
     // keep the first m -- every winner is a candidate.
-    sort_and_store(sh.cu.c.ckey, sh.cu.c.cid, int(C), m, k, orow, sh, nullptr);
+    sort_and_store(sh.cu.c.ckey, sh.cu.c.cid, int(C), m, k, orow, sh, nullptr, true, ranged,
+                   range);
     return;
   }
   bool try_count = true;
