@@ -136,10 +136,13 @@ __global__ __launch_bounds__(64 * NW, (gemv_tops_min_waves<NQ, NC, U, NW>())) vo
                                                                 float *__restrict__ scores,
                                                                 uint64_t *__restrict__ tops,
                                                                 int ngroups, int M) {
-  __shared__ float sc[NQ][64];
+  __shared__ float sc[NQ][64 + NW];  // the group's scores, then the merged tail's
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t g = blockIdx.x;
+  // The last workgroup also takes the final group when the launch leaves it
+  // out (at most NW rows: one per wave).
+  const bool tail = blockIdx.x == gridDim.x - 1 && int(gridDim.x) < ngroups;
 
   f4 qf[NQ][NC];
 #pragma unroll
@@ -181,11 +184,42 @@ __global__ __launch_bounds__(64 * NW, (gemv_tops_min_waves<NQ, NC, U, NW>())) vo
         if (lane == 0) sc[n][wave * RPW + it * U + u] = acc;
       }
   }
+  if (tail) {
+    const int64_t r = (g + 1) * 64 + wave;
+    if (r < A) {  // wave-uniform
+      f4 kf[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int e = 4 * (c * 64 + lane);
+        kf[c] = e < K ? load_f4_stream(kblk + r * K + e) : f4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) {
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          acc = __builtin_fmaf(qf[n][c].x, kf[c].x, acc);
+          acc = __builtin_fmaf(qf[n][c].y, kf[c].y, acc);
+          acc = __builtin_fmaf(qf[n][c].z, kf[c].z, acc);
+          acc = __builtin_fmaf(qf[n][c].w, kf[c].w, acc);
+        }
+        acc = butterfly_sum(acc);
+        if (lane == n && n < nq) scores[int64_t(n) * A + r] = acc;
+        if (lane == 0) sc[n][64 + wave] = acc;
+      }
+    }
+  }
   __syncthreads();
-  for (int n = wave; n < nq; n += NW) {  // wave-uniform
-    const uint32_t id = uint32_t(g * 64 + lane);
-    const uint32_t key = id < uint32_t(A) ? score_key(__float_as_uint(sc[n][lane])) : 0u;
-    publish_group_tops(key, id, M, tops + (int64_t(n) * ngroups + g) * M);
+  // Wave j publishes query j % nq's words of the group (j < nq) or of the
+  // merged tail group (nq <= j < 2 nq).
+  const int npub = tail ? 2 * nq : nq;
+  for (int j = wave; j < npub; j += NW) {  // wave-uniform
+    const int n = j < nq ? j : j - nq;
+    const int64_t gg = j < nq ? g : g + 1;
+    const uint32_t id = uint32_t(gg * 64 + lane);
+    const bool live = id < uint32_t(A) && (j < nq || lane < NW);
+    const uint32_t key = live ? score_key(__float_as_uint(sc[n][j < nq ? lane : 64 + lane])) : 0u;
+    publish_group_tops(key, id, M, tops + (int64_t(n) * ngroups + gg) * M);
   }
 }
 
@@ -203,8 +237,15 @@ hipError_t launch_gemv_tops_nc(const float *q, const float *kblk, int nq, int K,
   // 4096-float rows, whose operands need more than the 128 VGPRs of four
   // waves per SIMD.
   constexpr int NW = (NQ >= 4 || NC >= 16) ? 8 : 16;
-  scores_gemv_tops_kernel<NQ, NC, U, NW><<<ngroups, 64 * NW, 0, stream>>>(q, kblk, nq, K, A, scores, tops,
-                                                                 ngroups, M);
+  // With 16 waves per workgroup (two workgroups per CU, 512 at once), a final
+  // group of at most NW blocks -- the capacity-shaped rows of 2^n + 2 blocks
+  // end in one of 2 -- rides on the last full group's workgroup instead of
+  // queueing as workgroup 513 behind the first 512 (measured, select per
+  // call: two queries 21.2 -> 20.0 us, one query unchanged; with eight waves
+  // four workgroups fit per CU and nothing queues, so nothing is merged).
+  const bool merge = NW == 16 && ngroups >= 2 && A - 64 * (ngroups - 1) <= NW;
+  scores_gemv_tops_kernel<NQ, NC, U, NW><<<merge ? ngroups - 1 : ngroups, 64 * NW, 0, stream>>>(
+      q, kblk, nq, K, A, scores, tops, ngroups, M);
   return hipGetLastError();
 }
 

@@ -348,6 +348,9 @@ SELECT_CASES = [  # nq, heads, dim, active, k  (nq <= 8 with K <= 4096/nq fuse; 
     (9, 4, 128, 3000, 256), (1, 4, 128, 131073, 64), (40, 4, 128, 2000, 100), (8, 8, 128, 300, 30),
     # decode at large k: more published words than 8 per thread, up to 128 rank workgroups
     (1, 4, 128, 32770, 4096), (4, 4, 128, 32770, 2048), (2, 4, 128, 33793, 3000),
+    # a final group of 16, 1 and 17 blocks: the first two ride on the last full
+    # group's workgroup of the 16-wave fused scorer, the third has its own
+    (1, 4, 128, 1040, 64), (2, 4, 128, 32769, 512), (2, 4, 128, 1041, 64), (2, 4, 128, 80, 90),
 ]
 
 
@@ -365,6 +368,25 @@ def test_select_matches_separate_calls(nq, heads, dim, active, k):
     assert np.array_equal(i_sel, i_sep), "select's ids differ from qsa_block_topk"
     check_scores(s_sel, ORC.scores_f64(q, kb, active))
     assert np.array_equal(i_sel, ORC.topk(s_sel, k))
+
+
+@pytest.mark.parametrize("nq,active", [(1, 32770), (2, 1040), (1, 65)])
+def test_select_winners_in_merged_tail(nq, active):
+    """The best blocks sit in the final, partial group, whose scores and group
+    words the fused scorer's last workgroup produces besides its own group."""
+    from sparse_attention_kv_qsa_amd import qsa_block_select
+    q, kb = synth.make_random(nq, 4, 128, active, capacity=active + 2, seed=active + nq)
+    tail = np.arange(64 * ((active - 1) // 64), active)
+    kb[tail] = 3.0 * q[np.arange(len(tail)) % nq]  # these blocks score highest for their query
+    qt, kt = torch.from_numpy(q).cuda(), torch.from_numpy(kb).cuda()
+    k = 24
+    s, ids = qsa_block_select(qt, kt, k, active)
+    torch.cuda.synchronize()
+    s, ids = s.cpu().numpy(), ids.cpu().numpy()
+    check_scores(s, ORC.scores_f64(q, kb, active))
+    assert np.array_equal(ids, ORC.topk(s, k))
+    for n in range(nq):
+        assert set(tail[np.arange(len(tail)) % nq == n].tolist()) <= set(ids[n].tolist())
 
 
 def test_select_edges(gpu):
