@@ -187,28 +187,57 @@ __device__ __forceinline__ Threshold radix_select(TopkShared &sh, Visit &&visit,
 // counter `*count`, one LDS atomic per wave.  `visit` must visit every lane
 // of the wave the same number of times (all lanes active).  Writes past
 // `cap` are dropped; the counter still counts them.
-template <class Visit, class Pred>
+// Append the (id, key) pairs for which pred holds to LDS arrays at counter
+// `*count`, one LDS atomic per wave.  `visit` must visit every lane of the
+// wave the same number of times (all lanes active).  If a wave's pairs would
+// pass `cap`, that wave writes none of them; the counter still counts them.
+// PER_THREAD: each thread counts its own pairs (vector adds, no per-slot wave
+// operations), one prefix sum over the wave places them and each thread
+// appends its own -- fewer instructions per slot, more registers (used up to
+// 32 register slots per thread).  Otherwise a ballot per slot places them.
+// The order of the pairs differs between the two; no caller depends on it.
+template <bool PER_THREAD, class Visit, class Pred>
 __device__ __forceinline__ void compact(Visit &&visit, Pred &&pred, uint32_t *count, uint32_t *dkey,
                         uint32_t *did, uint32_t cap) {
   const int lane = threadIdx.x & 63;
-  uint32_t total = 0;
-  visit([&](uint32_t id, uint32_t key) { total += __popcll(__ballot(pred(id, key))); });
-  uint32_t base = 0;
-  if (lane == 0 && total) base = atomicAdd(count, total);
-  base = __builtin_amdgcn_readfirstlane(base);
-  visit([&](uint32_t id, uint32_t key) {
-    // Re-evaluate the predicate here rather than keep every slot's wave mask
-    // from the counting visit alive in scalar registers.
-    asm volatile("" : "+v"(key));
-    const bool p = pred(id, key);
-    const uint64_t bal = __ballot(p);
-    const uint32_t pos = base + lanes_below(bal);
-    if (p && pos < cap) {
-      dkey[pos] = key;
-      did[pos] = id;
-    }
-    base += __popcll(bal);
-  });
+  if constexpr (PER_THREAD) {
+    uint32_t mine = 0;
+    visit([&](uint32_t id, uint32_t key) { mine += pred(id, key) ? 1u : 0u; });
+    const uint32_t incl = wave_incl_scan(mine);
+    const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+    uint32_t base = 0;
+    if (lane == 0 && total) base = atomicAdd(count, total);
+    base = __builtin_amdgcn_readfirstlane(base);
+    if (base + total > cap) return;  // wave-uniform
+    uint32_t pos = base + incl - mine;
+    visit([&](uint32_t id, uint32_t key) {
+      // Re-evaluate the predicate rather than keep every slot's result alive.
+      asm volatile("" : "+v"(key));
+      if (pred(id, key)) {
+        dkey[pos] = key;
+        did[pos] = id;
+        ++pos;
+      }
+    });
+  } else {
+    uint32_t total = 0;
+    visit([&](uint32_t id, uint32_t key) { total += __popcll(__ballot(pred(id, key))); });
+    uint32_t base = 0;
+    if (lane == 0 && total) base = atomicAdd(count, total);
+    base = __builtin_amdgcn_readfirstlane(base);
+    if (base + total > cap) return;  // wave-uniform
+    visit([&](uint32_t id, uint32_t key) {
+      asm volatile("" : "+v"(key));
+      const bool p = pred(id, key);
+      const uint64_t bal = __ballot(p);
+      if (p) {
+        const uint32_t pos = base + lanes_below(bal);
+        dkey[pos] = key;
+        did[pos] = id;
+      }
+      base += __popcll(bal);
+    });
+  }
 }
 
 // Bitonic sort of P = W NT rank words (descending), W words per thread: word r
@@ -491,6 +520,13 @@ __device__ __forceinline__ void sort_and_store(uint32_t *skey, uint32_t *sid, in
   else sort_wide<4>(skey, sid, n, m, k, orow, xbuf);
 }
 
+// Register slots of width PER that lie inside every row the dispatcher gives
+// that width: rows longer than (next smaller width + 1) * NT.
+constexpr int topk_full_slots(int per) {
+  return per >= 64 ? 48 : per >= 47 ? 33 : per >= 32 ? 24 : per >= 23 ? 16 : per >= 15 ? 8
+       : per >= 7 ? 4 : per >= 3 ? 2 : per >= 1 ? 1 : 0;
+}
+
 template <int PER>
 struct RowKeys {
   uint32_t key[PER > 0 ? PER : 1];
@@ -505,6 +541,9 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
   const int lane = t & 63;
   const int wave = t >> 6;
   const int m = min(k, A);
+  // Up to 32 register slots per thread the leaner per-slot code fits the
+  // register file; the wider rows keep the code that needs fewer registers.
+  constexpr bool kLean = PER >= 0 && PER <= 32;
 
   if (m == 0) {  // no active blocks: every slot is padding
     for (int r = t; r < k; r += NT) orow[r] = -1;
@@ -543,10 +582,22 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
 #pragma unroll
     for (int j = 0; j < PER; ++j) rk.key[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, (j * NT + t) * 4, 0, 0);
     uint32_t xr = __builtin_amdgcn_raw_buffer_load_b32(rs, (PER * NT + t) * 4, 0, 0);
+    // Slots below kFull hold ids inside every row this width is chosen for
+    // (the dispatcher takes the smallest width that holds the row, so the
+    // row is longer than the next smaller width's slots): no id check there.
+    constexpr int kFull = kLean ? topk_full_slots(PER) : 0;
+    if (kFull > 0 && A >= kFull * NT) {  // workgroup-uniform; always true from the dispatcher
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      asm volatile("" : "+v"(rk.key[j]));
-      rk.key[j] = j * NT + t < A ? score_key(rk.key[j]) : 0u;
+      for (int j = 0; j < PER; ++j) {
+        asm volatile("" : "+v"(rk.key[j]));
+        rk.key[j] = (j < kFull || j * NT + t < A) ? score_key(rk.key[j]) : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        asm volatile("" : "+v"(rk.key[j]));
+        rk.key[j] = j * NT + t < A ? score_key(rk.key[j]) : 0u;
+      }
     }
     asm volatile("" : "+v"(xr));
     sh.extra[t] = PER * NT + t < A ? score_key(xr) : 0u;
@@ -658,7 +709,7 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
     ranged = true;
   }
 
-  compact(visit_row, [&](uint32_t, uint32_t key) { return key >= bound; }, &sh.ncand, sh.cu.c.ckey,
+  compact<kLean>(visit_row, [&](uint32_t, uint32_t key) { return key >= bound; }, &sh.ncand, sh.cu.c.ckey,
           sh.cu.c.cid, CAP);
   __syncthreads();
   const uint32_t C = sh.ncand;
@@ -682,13 +733,13 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
     };
     Threshold th;
     if (uint32_t(k) < C) th = radix_select(sh, visit_cand, uint32_t(k), padC - C, A);
-    compact(visit_cand, [&](uint32_t id, uint32_t key) { return key != 0u && th.wins(id, key); },
+    compact<kLean>(visit_cand, [&](uint32_t id, uint32_t key) { return key != 0u && th.wins(id, key); },
             &sh.nwin, sh.bkey, sh.bid, MAXK);
     try_count = !th.by_id && th.tied <= kBucketCap;
   } else {
     // Too many candidates for LDS: select over the whole row.
     const Threshold th = radix_select(sh, visit_row, uint32_t(k), n_sentinel, A);
-    compact(visit_row, [&](uint32_t id, uint32_t key) { return key != 0u && th.wins(id, key); },
+    compact<kLean>(visit_row, [&](uint32_t id, uint32_t key) { return key != 0u && th.wins(id, key); },
             &sh.nwin, sh.bkey, sh.bid, MAXK);
     try_count = !th.by_id && th.tied <= kBucketCap;
   }
