@@ -623,7 +623,12 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
       for (int base = 0; base < A; base += NT) f(uint32_t(base + tv), load_key(base + tv));
     }
   };
-  __syncthreads();
+  // No barrier here when the bound is taken: a thread reads back only its own
+  // extra slot, and the bound's barrier below orders the cleared histograms
+  // and counters before any use, so each wave starts on its keys as soon as
+  // its own loads arrive.
+  const bool take_bound = k < A && k <= 4 * NT;  // workgroup-uniform
+  if (!take_bound) __syncthreads();
 
   // Candidate bound.  Every thread's two (k > NT: four) largest keys over its
   // own slots are distinct elements of the row (or sentinels).  Each wave
@@ -638,7 +643,7 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
   uint32_t bound = 1u;
   KeyRange range{0u, 0u};  // the candidates' keys, set with the bound
   bool ranged = false;
-  if (k < A && k <= 4 * NT) {
+  if (take_bound) {
     // Up to k = NT each thread keeps its two largest keys, beyond that its
     // four (kw <= 64 or 256 values of the wave are then enough).
     const bool four = k > NT;  // workgroup-uniform
