@@ -26,12 +26,12 @@
 //      block id (lowest first) among keys == T, so ties go to the lower block
 //      id.  (If the candidates overflow LDS, the passes run over the
 //      register-resident row instead; the result is the same.)
-//   4. rank order (key desc, id asc).  Up to NT pairs: a counting rank --
-//      buckets by key, one prefix sum over the bucket counts, then a count of
-//      the larger words inside each pair's own bucket -- unless a bucket
-//      takes more than kBucketCap pairs (bulk ties); then, and beyond NT
-//      pairs, a bitonic sort: in registers with lane exchanges for strides
-//      < 64, through LDS above that.
+//   4. rank order (key desc, id asc): a counting rank -- buckets by key, one
+//      prefix sum over the bucket counts, then a count of the larger words
+//      inside each pair's own bucket (1, 2 or 4 pairs per thread) -- unless a
+//      bucket takes more than kBucketCap pairs (bulk ties); then a bitonic
+//      sort: in registers with lane exchanges for strides < 64, through LDS
+//      above that.
 #include <hip/hip_runtime.h>
 
 #include "qsa_device.h"
@@ -55,6 +55,7 @@ struct TopkShared {
   uint32_t wmin[NWAVES];       // per-wave candidate bound; per-wave smallest key of the counting rank
   uint32_t wmax[NWAVES];       // per-wave largest key of the counting rank
   uint32_t big;                // the counting rank met a bucket past its cap
+  uint32_t wsum[NWAVES];       // wave totals of the wide counting rank's prefix sum
   union {
     struct {
       uint32_t ckey[CAP];      // candidates: keys ...
@@ -444,6 +445,114 @@ __device__ __forceinline__ bool counting_rank_store(const uint32_t *skey, const 
   return true;
 }
 
+// The counting rank for NT < n <= W NT pairs (the winners of k > NT), W of
+// them per thread (pair t + j NT for j < W): W NT buckets, each thread owning
+// W consecutive ones in the prefix sum; the pairs are placed bucket by bucket
+// in the candidates' area (free once the winners are gathered).  The rest as
+// counting_rank_store.  Returns false, having stored nothing, when a bucket
+// receives more than kBucketCap pairs.  Every thread must call it.
+template <int W>
+__device__ __forceinline__ bool counting_rank_store_wide(const uint32_t *skey, const uint32_t *sid,
+                                                         int n, int m, int k,
+                                                         int *__restrict__ orow, TopkShared &sh) {
+  constexpr int NB = W * NT;  // <= the NWAVES * 256 words of hsub
+  constexpr int LGNB = W == 2 ? 11 : 12;
+  static_assert(NB <= NWAVES * 256 && (W == 2 || W == 4), "bucket counts live in hsub");
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  uint32_t key[W], id[W];
+  uint32_t hi = 0u, lo = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    const int i = t + j * NT;
+    const bool live = i < n;
+    key[j] = live ? skey[i] : 0u;
+    id[j] = live ? sid[i] : 0u;
+    if (live) {
+      hi = max(hi, key[j]);
+      lo = min(lo, key[j]);
+    }
+  }
+  hi = max(hi, lane_xor<1>(hi)); lo = min(lo, lane_xor<1>(lo));
+  hi = max(hi, lane_xor<2>(hi)); lo = min(lo, lane_xor<2>(lo));
+  hi = max(hi, lane_xor<4>(hi)); lo = min(lo, lane_xor<4>(lo));
+  hi = max(hi, lane_xor<8>(hi)); lo = min(lo, lane_xor<8>(lo));
+  hi = max(hi, lane_xor<16>(hi)); lo = min(lo, lane_xor<16>(lo));
+  hi = max(hi, lane_xor<32>(hi)); lo = min(lo, lane_xor<32>(lo));
+  uint32_t *cnt = &sh.hsub[0][0];  // bucket counts, then each bucket's first rank
+  if (lane == 0) {
+    sh.wmin[wave] = lo;
+    sh.wmax[wave] = hi;
+  }
+#pragma unroll
+  for (int j = 0; j < W; ++j) cnt[t + j * NT] = 0u;
+  if (t == 0) sh.big = 0u;
+  __syncthreads();
+  hi = 0u;
+  lo = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < NWAVES; ++w) {
+    hi = max(hi, sh.wmax[w]);
+    lo = min(lo, sh.wmin[w]);
+  }
+  const uint32_t span = hi - lo;
+  const int shift = max(0, 32 - __builtin_clz(span | 1u) - LGNB);
+  uint32_t b[W], within[W];
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    b[j] = (hi - key[j]) >> shift;
+    within[j] = 0u;
+    if (t + j * NT < n) {
+      within[j] = atomicAdd(&cnt[b[j]], 1u);
+      if (within[j] >= kBucketCap) sh.big = 1u;
+    }
+  }
+  __syncthreads();
+  if (sh.big) return false;
+  uint32_t c[W], local = 0u;
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    c[j] = cnt[W * t + j];
+    local += c[j];
+  }
+  uint32_t total;
+  uint32_t first = block_excl_scan(local, sh.wsum, total);
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    cnt[W * t + j] = first;
+    first += c[j];
+  }
+  uint64_t *sw = sh.cu.xbuf;  // CAP words >= n + 3
+  if (t < 4) sw[n + t] = 0ull;  // the rank loop reads up to three words past the last bucket
+  __syncthreads();
+  uint32_t start[W], end[W];
+  uint64_t word[W];
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    word[j] = rank_word(key[j], id[j]);
+    start[j] = end[j] = 0u;
+    if (t + j * NT < n) {
+      start[j] = cnt[b[j]];
+      end[j] = b[j] + 1 < uint32_t(NB) ? cnt[b[j] + 1] : uint32_t(n);
+      sw[start[j] + within[j]] = word[j];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    if (t + j * NT < n) {
+      uint32_t r = start[j];
+      for (uint32_t q = start[j]; q < end[j]; q += 4)
+        r += uint32_t(sw[q] > word[j]) + uint32_t(sw[q + 1] > word[j]) +
+             uint32_t(sw[q + 2] > word[j]) + uint32_t(sw[q + 3] > word[j]);
+      if (r < uint32_t(m)) orow[r] = int(id[j]);
+    }
+  }
+  for (int r = m + t; r < k; r += NT) orow[r] = -1;
+  return true;
+}
+
 // Rank-order sort of the n (key, id) pairs in LDS arrays skey/sid, then the
 // store of one row of ids: the first m in rank order, then -1 up to k.
 // `wbuf` is 2 NT words of LDS scratch; `xbuf`, 2 MAXK words, is used only
@@ -516,8 +625,13 @@ __device__ __forceinline__ void sort_and_store(uint32_t *skey, uint32_t *sid, in
     return;
   }
   // P in (NT, MAXK]: W = P / NT words per thread.
-  if (P == 2 * NT) sort_wide<2>(skey, sid, n, m, k, orow, xbuf);
-  else sort_wide<4>(skey, sid, n, m, k, orow, xbuf);
+  if (P == 2 * NT) {
+    if (try_count && counting_rank_store_wide<2>(skey, sid, n, m, k, orow, sh)) return;
+    sort_wide<2>(skey, sid, n, m, k, orow, xbuf);
+  } else {
+    if (try_count && counting_rank_store_wide<4>(skey, sid, n, m, k, orow, sh)) return;
+    sort_wide<4>(skey, sid, n, m, k, orow, xbuf);
+  }
 }
 
 // Register slots of width PER that lie inside every row the dispatcher gives
