@@ -123,16 +123,21 @@ def parse_args():
     return p.parse_args()
 
 
-def source_digest(path: str) -> str:
-    """Hash of a kernel's source file (the counters are void once it changes)."""
+def build_digest(path: str) -> str:
+    """Hash of a kernel's source file and of the library's compiler flags: the
+    counters taken on a build are void once either changes."""
     import hashlib
+    from sparse_attention_kv_qsa_amd.build import HIPCC_FLAGS
+    h = hashlib.sha256()
     with open(os.path.join(CSRC, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        h.update(f.read())
+    h.update(b"\0" + " ".join(HIPCC_FLAGS).encode())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(path: str, workload: str):
     """HBM bytes per scorer launch from committed counter runs, if they were
-    taken on the current source of that scorer; else None."""
+    taken on the current source and build flags of that scorer; else None."""
     src, summary = SCORERS[path]
     fname = os.path.join(ROOT, "profiles", summary)
     if workload != synth.HEADLINE or not os.path.exists(fname):
@@ -142,7 +147,7 @@ def read_traffic(path: str, workload: str):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             kv[key.strip()] = val.strip()
-    if kv.get("scorer_source_sha256_16") != source_digest(src):
+    if kv.get("scorer_build_sha256_16") != build_digest(src):
         return None
     try:
         return int(kv["hbm_bytes_per_launch"])
