@@ -127,11 +127,11 @@ def build_digest(path: str) -> str:
     """Hash of a kernel's source file and of the library's compiler flags: the
     counters taken on a build are void once either changes."""
     import hashlib
-    from sparse_attention_kv_qsa_amd.build import HIPCC_FLAGS
+    from sparse_attention_kv_qsa_amd.build import flags_for
     h = hashlib.sha256()
     with open(os.path.join(CSRC, path), "rb") as f:
         h.update(f.read())
-    h.update(b"\0" + " ".join(HIPCC_FLAGS).encode())
+    h.update(b"\0" + " ".join(flags_for(os.path.join(CSRC, path))).encode())
     return h.hexdigest()[:16]
 
 

@@ -33,8 +33,8 @@ FIELDS = {
 
 
 def compile_remarks(path: str, outdir: str) -> list[dict]:
-    from sparse_attention_kv_qsa_amd.build import ARCH, HIPCC_FLAGS
-    flags = [f for f in HIPCC_FLAGS if f not in ("-shared",)]
+    from sparse_attention_kv_qsa_amd.build import ARCH, flags_for
+    flags = flags_for(path)
     cmd = [HIPCC, *flags, f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}", "-c", path,
            "--offload-device-only", "-Rpass-analysis=kernel-resource-usage",
            "-o", os.path.join(outdir, os.path.basename(path) + ".o")]
