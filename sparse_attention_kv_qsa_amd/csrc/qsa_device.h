@@ -7,13 +7,15 @@
 namespace qsa {
 
 // Order-preserving map of an fp32 score (given as its bits) to uint32: a
-// larger score gives a larger key.  -0.0 is folded onto +0.0.  Key 0 is kept
-// free as the "no block" sentinel; the one score that would map there is a
-// NaN (whose rank is unspecified), so it moves to 1.
+// larger score gives a larger key.  A score with the sign bit clear maps to
+// u + 2^31 (its bits with the sign bit set); a negative one to 2^32 - u (the
+// two's complement negation), which reverses the order of the magnitudes and
+// sends -0.0 to 2^31, the key of +0.0.  The negative range lands on
+// [1, 2^31], so key 0 stays free as the "no block" sentinel.  Three vector
+// instructions (negate, sign test, select with the sign set by a source
+// modifier).
 __device__ __forceinline__ uint32_t score_key(uint32_t u) {
-  if (u == 0x80000000u) u = 0u;
-  const uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return key == 0u ? 1u : key;
+  return int32_t(u) < 0 ? 0u - u : (u | 0x80000000u);
 }
 
 // Rank word of a (key, id) pair: a larger word ranks first (larger key, or

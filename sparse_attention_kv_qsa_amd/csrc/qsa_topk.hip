@@ -34,6 +34,9 @@
 //      above that.
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
+#include <type_traits>
+
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -197,11 +200,21 @@ __device__ __forceinline__ Threshold radix_select(TopkShared &sh, Visit &&visit,
 // appends its own -- fewer instructions per slot, more registers (used up to
 // 32 register slots per thread).  Otherwise a ballot per slot places them.
 // The order of the pairs differs between the two; no caller depends on it.
-template <bool PER_THREAD, class Visit, class Pred>
+//
+// The per-thread form evaluates the predicate twice (count, then append)
+// rather than keep every slot's result alive (two scalar registers a slot).
+// To keep the compiler from reusing the first results, `hide` runs between
+// the passes: it hides a value the predicate reads (one register move); the
+// default hides each key instead (a move per slot).
+struct HideKeys {
+  __device__ void operator()() const {}
+};
+template <bool PER_THREAD, class Visit, class Pred, class Hide = HideKeys>
 __device__ __forceinline__ void compact(Visit &&visit, Pred &&pred, uint32_t *count, uint32_t *dkey,
-                        uint32_t *did, uint32_t cap) {
+                        uint32_t *did, uint32_t cap, Hide &&hide = Hide{}) {
   const int lane = threadIdx.x & 63;
   if constexpr (PER_THREAD) {
+    constexpr bool kHideKeys = std::is_same_v<std::decay_t<Hide>, HideKeys>;
     uint32_t mine = 0;
     visit([&](uint32_t id, uint32_t key) { mine += pred(id, key) ? 1u : 0u; });
     const uint32_t incl = wave_incl_scan(mine);
@@ -210,14 +223,17 @@ __device__ __forceinline__ void compact(Visit &&visit, Pred &&pred, uint32_t *co
     if (lane == 0 && total) base = atomicAdd(count, total);
     base = __builtin_amdgcn_readfirstlane(base);
     if (base + total > cap) return;  // wave-uniform
-    uint32_t pos = base + incl - mine;
+    hide();
+    // One LDS address per thread, advanced per pair; the id array's offset
+    // from the key array is a constant (the store's immediate offset).
+    uint32_t *kp = dkey + (base + incl - mine);
+    const ptrdiff_t idoff = did - dkey;
     visit([&](uint32_t id, uint32_t key) {
-      // Re-evaluate the predicate rather than keep every slot's result alive.
-      asm volatile("" : "+v"(key));
+      if constexpr (kHideKeys) asm volatile("" : "+v"(key));
       if (pred(id, key)) {
-        dkey[pos] = key;
-        did[pos] = id;
-        ++pos;
+        kp[0] = key;
+        kp[idoff] = id;
+        ++kp;
       }
     });
   } else {
@@ -690,17 +706,27 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
   uint32_t n_sentinel = 0;
   if constexpr (PER >= 0) {
     n_sentinel = uint32_t((PER + 1) * NT - A);
+    // Slots below kFull hold ids inside every row this width is chosen for
+    // (the dispatcher takes the smallest width that holds the row, so the
+    // row is longer than the next smaller width's slots): no id check there,
+    // and their loads take the slot's offset from a scalar register (one
+    // vector offset for all of them instead of one vector add per slot).
+    constexpr int kFull = kLean ? topk_full_slots(PER) : 0;
+    const bool full = kFull > 0 && A >= kFull * NT;  // workgroup-uniform; always true from the dispatcher
+    if (full) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        rk.key[j] = j < kFull ? __builtin_amdgcn_raw_buffer_load_b32(rs, t * 4, j * NT * 4, 0)
+                              : __builtin_amdgcn_raw_buffer_load_b32(rs, (j * NT + t) * 4, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) rk.key[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, (j * NT + t) * 4, 0, 0);
+    }
+    uint32_t xr = __builtin_amdgcn_raw_buffer_load_b32(rs, (PER * NT + t) * 4, 0, 0);
     // All loads first (raw bits), then the transform: the empty asm makes each
     // loaded value live unconditionally, so the compiler cannot sink a load
     // into the id < A branch and wait on it there.
-#pragma unroll
-    for (int j = 0; j < PER; ++j) rk.key[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, (j * NT + t) * 4, 0, 0);
-    uint32_t xr = __builtin_amdgcn_raw_buffer_load_b32(rs, (PER * NT + t) * 4, 0, 0);
-    // Slots below kFull hold ids inside every row this width is chosen for
-    // (the dispatcher takes the smallest width that holds the row, so the
-    // row is longer than the next smaller width's slots): no id check there.
-    constexpr int kFull = kLean ? topk_full_slots(PER) : 0;
-    if (kFull > 0 && A >= kFull * NT) {  // workgroup-uniform; always true from the dispatcher
+    if (full) {
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         asm volatile("" : "+v"(rk.key[j]));
@@ -762,13 +788,16 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
     // four (kw <= 64 or 256 values of the wave are then enough).
     const bool four = k > NT;  // workgroup-uniform
     uint32_t v0 = 0u, v1 = 0u, v2 = 0u, v3 = 0u;  // this thread's largest keys, descending
+    // The median of three: with v0 >= v1 the new second largest is
+    // med3(v0, x, v1); the compiler emits one v_med3_u32 for this form.
+    auto med3 = [](uint32_t a, uint32_t b, uint32_t c) { return max(min(a, b), min(max(a, b), c)); };
     auto take2 = [&](uint32_t x) {
-      v1 = max(v1, min(v0, x));
+      v1 = med3(v0, x, v1);
       v0 = max(v0, x);
     };
     auto take4 = [&](uint32_t x) {
-      v3 = max(v3, min(v2, x));
-      v2 = max(v2, min(v1, x));
+      v3 = med3(v2, x, v3);
+      v2 = med3(v1, x, v2);
       take2(x);
     };
     if constexpr (PER >= 0) {
@@ -829,7 +858,7 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
   }
 
   compact<kLean>(visit_row, [&](uint32_t, uint32_t key) { return key >= bound; }, &sh.ncand, sh.cu.c.ckey,
-          sh.cu.c.cid, CAP);
+          sh.cu.c.cid, CAP, [&] { asm volatile("" : "+v"(bound)); });
   __syncthreads();
   const uint32_t C = sh.ncand;
 
