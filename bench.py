@@ -91,7 +91,12 @@ CSRC = os.path.join(ROOT, "sparse_attention_kv_qsa_amd", "csrc")
 SCORERS = {
     "fp32": ("qsa_scores.hip", "traffic_scores_mfma_prompt-128k.txt"),
     "bf16x3": ("qsa_scores_bf16x3.hip", "traffic_scores_bf16x3_prompt-128k.txt"),
+    "f16x2": ("qsa_scores_f16x2.hip", "traffic_scores_f16x2_prompt-128k.txt"),
 }
+# Split scorers: matrix products per fp32 product, kernel, matrix-core input type.
+SPLITS = {"bf16x3": (6, "scores_bf16x3_kernel", "bf16"), "f16x2": (3, "scores_f16x2_kernel", "f16")}
+# The scorer the library's AUTO mode takes for more than 8 queries.
+AUTO_SPLIT = "f16x2"
 
 
 def parse_args():
@@ -104,7 +109,7 @@ def parse_args():
                    help="blocks selected per query (default: the workload's k)")
     p.add_argument("--copies", type=int, default=6,
                    help="input copies rotated over the steps (defeats cache reuse)")
-    p.add_argument("--scores-mode", default="auto", choices=["auto", "fp32", "bf16x3"],
+    p.add_argument("--scores-mode", default="auto", choices=["auto", "fp32", "bf16x3", "f16x2"],
                    help="precision mode of qsa_block_scores_ex (auto = the library default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--repeats", type=int, default=7,
@@ -468,10 +473,10 @@ def main():
     score_s = score_ms * 1e-3
     # The kernel the library runs for this shape and mode (mirrors its dispatch).
     gemv_ok = w.nq <= 8 and w.nq * -(-w.K // 256) <= 16
-    if gemv_ok and mode != "bf16x3":
+    if gemv_ok and mode not in SPLITS:
         path = "gemv"
     else:
-        path = "bf16x3" if mode in ("auto", "bf16x3") else "fp32"
+        path = AUTO_SPLIT if mode == "auto" else mode
     if path == "gemv":
         nbytes = 4.0 * (w.active * w.K + w.nq * w.K + w.nq * w.active)
         gbs = nbytes / score_s / 1e9
@@ -484,13 +489,15 @@ def main():
         roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tf / PEAK_FP32_MFMA_TFLOPS, 4),
                 "traffic": read_traffic(path, w.name),
-                "kernel": "scores_mfma_kernel" if path == "fp32" else "scores_bf16x3_kernel",
+                "kernel": "scores_mfma_kernel" if path == "fp32" else SPLITS[path][1],
                 "flop_per_launch": int(flop), "ms_per_launch": round(score_ms, 5)}
-        if path == "bf16x3":
-            # The split forms six bf16 slice products per fp32 product.
-            roof["bf16_pipe"] = {"achieved": round(6 * tf, 2), "peak": PEAK_BF16_MFMA_TFLOPS,
-                                 "unit": "TFLOP/s", "frac": round(6 * tf / PEAK_BF16_MFMA_TFLOPS, 4),
-                                 "flop_per_launch": int(6 * flop)}
+        if path in SPLITS:
+            # The split forms n bf16 (fp16) piece products per fp32 product;
+            # both have the same dense matrix-core peak.
+            n, _, ty = SPLITS[path]
+            roof[f"{ty}_pipe"] = {"achieved": round(n * tf, 2), "peak": PEAK_BF16_MFMA_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(n * tf / PEAK_BF16_MFMA_TFLOPS, 4),
+                                  "flop_per_launch": int(n * flop)}
     topk_bytes = 4.0 * (w.nq * w.active + w.nq * w.k)
     sbytes = select_bytes(w)
 
@@ -506,7 +513,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": (round(value / (256 * 32770 / (PAGES_SELECT_MS * 1e-3)), 3)
                         if w.name == synth.HEADLINE else None),
-        "dtype": "bf16x3" if path == "bf16x3" else "f32",
+        "dtype": path if path in SPLITS else "f32",
         "data": "synthetic (seeded N(0,1) fp32 queries and block summaries, planted needles)",
         "config": {
             "workload": (f"{w.name}: {w.nq} queries x {w.active} active blocks "

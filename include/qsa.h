@@ -136,7 +136,7 @@ int qsa_block_topk(const float *scores, int nq, int active_blocks, int k, int *i
  *
  *   QSA_SCORES_AUTO    the library's choice (what qsa_block_scores does):
  *                      nq <= 8 -> fp32 per-block dot products (bandwidth-bound);
- *                      larger nq -> QSA_SCORES_BF16X3.
+ *                      larger nq -> QSA_SCORES_F16X2.
  *   QSA_SCORES_FP32    fp32 arithmetic throughout: the dot-product kernel for
  *                      nq <= 8, fp32 matrix-core (MFMA) tiles otherwise.
  *   QSA_SCORES_BF16X3  bf16 matrix cores on an exact three-way split of every
@@ -147,6 +147,20 @@ int qsa_block_topk(const float *scores, int nq, int active_blocks, int k, int *i
  *                      dispatch", What item 2).  The dropped products are below
  *                      2^-24 of each term, so the error against FP64 is of the
  *                      same order as fp32 arithmetic's.
+ *   QSA_SCORES_F16X2   fp16 matrix cores on a two-piece split: every row (a
+ *                      query or a block summary) is scaled by a power of two
+ *                      fixed by its first 32 elements (their largest magnitude
+ *                      lands in [2^8, 2^9)), each scaled element is cut into
+ *                      binary16 hi + lo (both rounded to nearest; 22
+ *                      significant bits), and a product sums hi*hi (own fp32
+ *                      accumulator) and hi*lo + lo*hi, scaled back exactly.
+ *                      The same split principle as QSA_SCORES_BF16X3 with
+ *                      wider pieces: three matrix products instead of six,
+ *                      error of the same order.  A score whose scaled pieces
+ *                      would leave binary16's range (an element more than 2^7
+ *                      times its row's first-step maximum) is computed again
+ *                      from its two rows in FP64; so is any score of a
+ *                      non-finite input.
  *
  * Every mode keeps each score's arithmetic independent of the block's
  * position.  Other arguments, layouts and errors as qsa_block_scores; an
@@ -155,6 +169,7 @@ int qsa_block_topk(const float *scores, int nq, int active_blocks, int k, int *i
 #define QSA_SCORES_AUTO 0
 #define QSA_SCORES_FP32 1
 #define QSA_SCORES_BF16X3 2
+#define QSA_SCORES_F16X2 3
 int qsa_block_scores_ex(const float *q, const float *kblk, int nq, int heads, int dim,
                         int active_blocks, float *scores, int mode, void *stream);
 

@@ -26,9 +26,10 @@ QSA_MAX_HEAD_DIM = 4096
 TOPK_MAX_K = 4096
 MAX_ACTIVE_BLOCKS = 1 << 28
 TOPK_FEW_ROWS = 16
-QSA_SCORES_AUTO, QSA_SCORES_FP32, QSA_SCORES_BF16X3 = 0, 1, 2
+QSA_SCORES_AUTO, QSA_SCORES_FP32, QSA_SCORES_BF16X3, QSA_SCORES_F16X2 = 0, 1, 2, 3
 QSA_ATTN_MAX_DIM = 128
-SCORE_MODES = {"auto": QSA_SCORES_AUTO, "fp32": QSA_SCORES_FP32, "bf16x3": QSA_SCORES_BF16X3}
+SCORE_MODES = {"auto": QSA_SCORES_AUTO, "fp32": QSA_SCORES_FP32, "bf16x3": QSA_SCORES_BF16X3,
+               "f16x2": QSA_SCORES_F16X2}
 
 # Entry points declared in include/qsa.h: name -> (restype, argtypes).
 _VP, _I = ctypes.c_void_p, ctypes.c_int
@@ -114,7 +115,7 @@ def qsa_block_scores_ex(q: torch.Tensor, kblk: torch.Tensor, active_blocks: int 
     """Scores [nq, active_blocks] of q [nq, heads, dim] against kblk [C, heads, dim].
 
     Only rows [0, active_blocks) of kblk are read (default: all C rows).
-    mode: "auto" | "fp32" | "bf16x3" (or the QSA_SCORES_* integer).
+    mode: "auto" | "fp32" | "bf16x3" | "f16x2" (or the QSA_SCORES_* integer).
     """
     _require_gpu_f32("q", q, 3)
     _require_gpu_f32("kblk", kblk, 3)

@@ -14,7 +14,7 @@ static_assert(QSA_TOPK_FEW_ROWS == qsa::kWideMaxRows, "header and kernels disagr
 static_assert(QSA_NOALLOC_SCRATCH_BYTES == qsa::kNoAllocScratchBytes,
               "header and kernels disagree on the static scratch size");
 static_assert(QSA_SCORES_AUTO == qsa::kScoresAuto && QSA_SCORES_FP32 == qsa::kScoresFp32 &&
-                  QSA_SCORES_BF16X3 == qsa::kScoresBf16x3,
+                  QSA_SCORES_BF16X3 == qsa::kScoresBf16x3 && QSA_SCORES_F16X2 == qsa::kScoresF16x2,
               "header and kernels disagree on the precision modes");
 
 namespace {
@@ -34,7 +34,8 @@ extern "C" int qsa_block_scores_ex(const float *q, const float *kblk, int nq, in
   if (active_blocks > QSA_MAX_ACTIVE_BLOCKS) return QSA_ERR_SHAPE;
   const int64_t K = int64_t(heads) * dim;
   if (K < 4 || K % 4 != 0 || K > QSA_MAX_HEAD_DIM) return QSA_ERR_SHAPE;
-  if (mode != QSA_SCORES_AUTO && mode != QSA_SCORES_FP32 && mode != QSA_SCORES_BF16X3)
+  if (mode != QSA_SCORES_AUTO && mode != QSA_SCORES_FP32 && mode != QSA_SCORES_BF16X3 &&
+      mode != QSA_SCORES_F16X2)
     return QSA_ERR_MODE;
   if (nq == 0 || active_blocks == 0) return QSA_OK;
   if (!q || !kblk || !scores) return QSA_ERR_NULL;

@@ -20,6 +20,7 @@ constexpr int kGemvMaxQueries = 8;
 constexpr int kScoresAuto = 0;
 constexpr int kScoresFp32 = 1;
 constexpr int kScoresBf16x3 = 2;
+constexpr int kScoresF16x2 = 3;
 
 // Scores of nq queries against active_blocks summaries, K = heads*dim fp32
 // elements each, with the given precision mode (QSA_SCORES_* of qsa.h).
@@ -30,6 +31,11 @@ hipError_t launch_block_scores(const float *q, const float *kblk, int nq, int K,
 // fp32 operand (six slice products; any nq).
 hipError_t launch_block_scores_bf16x3(const float *q, const float *kblk, int nq, int K,
                                       int active_blocks, float *scores, hipStream_t stream);
+
+// The same scores on fp16 matrix cores with a scaled two-piece split of each
+// fp32 operand (three piece products; any nq).
+hipError_t launch_block_scores_f16x2(const float *q, const float *kblk, int nq, int K,
+                                     int active_blocks, float *scores, hipStream_t stream);
 
 // fp32 scores: the dot-product kernel for nq <= kGemvMaxQueries (and K that
 // fits its registers), else fp32 MFMA tiles.

@@ -529,12 +529,15 @@ hipError_t launch_block_scores_fp32(const float *q, const float *kblk, int nq, i
 }
 
 // Mode dispatch (modes of include/qsa.h).  AUTO: few queries are bandwidth-
-// bound and take the fp32 dot-product kernel; larger batches take the bf16x3
-// split MFMA tiles, whose error against FP64 is of the same order as the fp32
-// MFMA path's at 2.7x its throughput.
+// bound and take the fp32 dot-product kernel; larger batches take the fp16
+// two-piece split MFMA tiles, whose error against FP64 is of the same order
+// as the fp32 MFMA path's (prompt-128k scorer: 47.5 us against 62.5 us for
+// the bf16 three-way split and 91 us for fp32 MFMA).
 hipError_t launch_block_scores(const float *q, const float *kblk, int nq, int K, int A,
                                float *scores, int mode, hipStream_t stream) {
-  if (mode == kScoresBf16x3 || (mode == kScoresAuto && !gemv_fits(nq, K)))
+  if (mode == kScoresF16x2 || (mode == kScoresAuto && !gemv_fits(nq, K)))
+    return launch_block_scores_f16x2(q, kblk, nq, K, A, scores, stream);
+  if (mode == kScoresBf16x3)
     return launch_block_scores_bf16x3(q, kblk, nq, K, A, scores, stream);
   return launch_block_scores_fp32(q, kblk, nq, K, A, scores, stream);
 }

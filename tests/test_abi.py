@@ -53,8 +53,9 @@ def test_binding_covers_the_header():
     assert mac["QSA_ERR_NOMEM"] == binding.QSA_ERR_NOMEM
     assert mac["QSA_ERR_SCRATCH"] == binding.QSA_ERR_SCRATCH
     assert mac["QSA_NOALLOC_SCRATCH_BYTES"] == binding.QSA_NOALLOC_SCRATCH_BYTES
-    assert (mac["QSA_SCORES_AUTO"], mac["QSA_SCORES_FP32"], mac["QSA_SCORES_BF16X3"]) == (
-        binding.QSA_SCORES_AUTO, binding.QSA_SCORES_FP32, binding.QSA_SCORES_BF16X3)
+    assert (mac["QSA_SCORES_AUTO"], mac["QSA_SCORES_FP32"], mac["QSA_SCORES_BF16X3"],
+            mac["QSA_SCORES_F16X2"]) == (binding.QSA_SCORES_AUTO, binding.QSA_SCORES_FP32,
+                                         binding.QSA_SCORES_BF16X3, binding.QSA_SCORES_F16X2)
     assert mac["QSA_MAX_HEAD_DIM"] == binding.QSA_MAX_HEAD_DIM
     assert mac["QSA_ATTN_MAX_DIM"] == binding.QSA_ATTN_MAX_DIM
 
@@ -109,7 +110,7 @@ def test_block_scores_argument_checks(lib, args, status):
     assert lib.qsa_block_scores(*args, None) == status
 
 
-@pytest.mark.parametrize("mode,status", [(0, 0), (1, 0), (2, 0), (3, 6), (-1, 6)])
+@pytest.mark.parametrize("mode,status", [(0, 0), (1, 0), (2, 0), (3, 0), (4, 6), (-1, 6)])
 def test_block_scores_ex_mode_check(lib, mode, status):
     # a valid mode on an empty call is a no-op; an unknown mode is rejected first
     assert lib.qsa_block_scores_ex(None, None, 0, 4, 128, 10, None, mode, None) == status

@@ -40,7 +40,7 @@ def gpu():
     return lib
 
 
-MODES = ["fp32", "bf16x3"]  # "auto" is one of these for every shape
+MODES = ["fp32", "bf16x3", "f16x2"]  # "auto" is one of these for every shape
 
 
 def gpu_scores(q: np.ndarray, kblk: np.ndarray, active: int, mode="auto") -> np.ndarray:
@@ -158,6 +158,69 @@ def test_scores_deterministic_and_position_invariant(mode):
         for c in range(4):
             cols = s1[:, assign == c]
             assert np.all(cols == cols[:, :1]), "identical summaries scored differently"
+
+
+def test_f16x2_power_of_two_scaling_exact():
+    """The fp16 split scales every row by a power of two fixed by the row's
+    own data, so scaling a query or a block summary by 2^a scales its scores
+    by exactly 2^a (no result near the subnormal or overflow range here),
+    whatever the magnitude: rows at 2^-100 and 2^90 score like unit rows."""
+    rng = np.random.default_rng(21)
+    nq, a = 130, 197  # a ragged query tile and a narrow ragged column (197 % 64 = 5)
+    q = rng.standard_normal((nq, 4, 128)).astype(np.float32)
+    kb = rng.standard_normal((a, 4, 128)).astype(np.float32)
+    s = gpu_scores(q, kb, a, "f16x2")
+    check_scores(s, ORC.scores_f64(q, kb, a))
+    eq = rng.integers(-60, 60, nq)
+    eb = rng.integers(-60, 40, a)
+    eq[:3], eb[:3] = (-100, 90, 0), (0, -100, 88)
+    q2 = np.ascontiguousarray(np.ldexp(q, eq[:, None, None]).astype(np.float32))
+    kb2 = np.ascontiguousarray(np.ldexp(kb, eb[:, None, None]).astype(np.float32))
+    ok = np.abs(eq[:, None] + eb[None, :]) < 100  # products stay normal fp32 numbers
+    s2 = gpu_scores(q2, kb2, a, "f16x2")
+    want = np.ldexp(s.astype(np.float64), eq[:, None] + eb[None, :])
+    assert np.array_equal(s2[ok].astype(np.float64), want[ok])
+
+
+def test_f16x2_range_fallback():
+    """Rows with an element more than 2^7 times their first-step maximum
+    would overflow a binary16 piece: their scores are computed from the two
+    rows in FP64 (one rounding), identical wherever the block sits; rows
+    whose first step is all zeros stay unscaled; a non-finite input gives
+    non-finite scores in its row and column only."""
+    rng = np.random.default_rng(22)
+    nq, a = 140, 300
+    q = rng.standard_normal((nq, 4, 128)).astype(np.float32)
+    kb = rng.standard_normal((a, 4, 128)).astype(np.float32)
+    kb[3, 2, 5] = 3.0e5          # block 3: far above its first 32 elements
+    kb[299] = kb[3]              # the same summary in the narrow ragged column
+    kb[64] = kb[3]               # ... and in another full tile
+    q[7, 3, 100] = -2.0e6        # query 7 likewise
+    q[135] = q[7]                # a copy in the ragged query tile
+    kb[10, 0, :32] = 0.0         # first step all zeros: unscaled
+    kb[11, :, :] = 0.0
+    kb[11, 3, 127] = 5.0e4
+    s = gpu_scores(q, kb, a, "f16x2")
+    s64 = ORC.scores_f64(q, kb, a)
+    assert np.all(np.isfinite(s))
+    for c in (3, 64, 299):
+        assert np.array_equal(s[:, c], s[:, 3])
+    assert np.array_equal(s[7], s[135])
+    # the fallback's scores: FP64 sum rounded once
+    fb = np.zeros(s.shape, bool)
+    fb[:, [3, 64, 299]] = True
+    fb[[7, 135], :] = True
+    assert np.all(np.abs(s[fb] - s64[fb]) <= np.spacing(np.abs(s[fb]).astype(np.float32)))
+    # the other rows and columns within the gate on their own
+    rows = np.setdiff1d(np.arange(nq), [7, 135])
+    cols = np.setdiff1d(np.arange(a), [3, 64, 299])
+    check_scores(s[np.ix_(rows, cols)], s64[np.ix_(rows, cols)])
+    q3 = q.copy()
+    q3[5, 1, 7] = np.inf
+    s3 = gpu_scores(q3, kb, a, "f16x2")
+    assert not np.any(np.isfinite(s3[5]))
+    others = np.arange(nq) != 5
+    assert np.array_equal(s3[others], s[others])
 
 
 def test_scores_canary_untouched(gpu):
@@ -449,7 +512,7 @@ def margins(s, s64, ids, k):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("mode", ["auto", "fp32", "select"])
+@pytest.mark.parametrize("mode", ["auto", "fp32", "bf16x3", "select"])
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_workload_parity(name, mode):
     w = synth.WORKLOADS[name]

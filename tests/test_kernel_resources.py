@@ -81,7 +81,7 @@ def kernels():
 
 def test_every_kernel_reports(kernels):
     names = {r["name"].split("<")[0] for r in kernels}
-    for k in ("scores_bf16x3_kernel", "scores_mfma_kernel", "scores_gemv_kernel",
+    for k in ("scores_bf16x3_kernel", "scores_f16x2_kernel", "scores_mfma_kernel", "scores_gemv_kernel",
               "scores_gemv_tops_kernel", "topk_kernel", "group_tops_kernel", "wide_rank_kernel",
               "attn_chunk_kernel", "attn_chunk_i8_kernel", "attn_merge_kernel"):
         assert k in names, f"no resource remarks for {k}"
