@@ -182,7 +182,8 @@ def test_f16x2_power_of_two_scaling_exact():
     assert np.array_equal(s2[ok].astype(np.float64), want[ok])
 
 
-def test_f16x2_range_fallback():
+@pytest.mark.parametrize("heads,dim", [(4, 128), (3, 20)])  # K = 512 (LDS-staged queries), 60
+def test_f16x2_range_fallback(heads, dim):
     """Rows with an element more than 2^7 times their first-step maximum
     would overflow a binary16 piece: their scores are computed from the two
     rows in FP64 (one rounding), identical wherever the block sits; rows
@@ -190,16 +191,16 @@ def test_f16x2_range_fallback():
     non-finite scores in its row and column only."""
     rng = np.random.default_rng(22)
     nq, a = 140, 300
-    q = rng.standard_normal((nq, 4, 128)).astype(np.float32)
-    kb = rng.standard_normal((a, 4, 128)).astype(np.float32)
+    q = rng.standard_normal((nq, heads, dim)).astype(np.float32)
+    kb = rng.standard_normal((a, heads, dim)).astype(np.float32)
     kb[3, 2, 5] = 3.0e5          # block 3: far above its first 32 elements
     kb[299] = kb[3]              # the same summary in the narrow ragged column
     kb[64] = kb[3]               # ... and in another full tile
-    q[7, 3, 100] = -2.0e6        # query 7 likewise
+    q[7, -1, -3] = -2.0e6        # query 7 likewise
     q[135] = q[7]                # a copy in the ragged query tile
-    kb[10, 0, :32] = 0.0         # first step all zeros: unscaled
+    kb[10].reshape(-1)[:32] = 0.0  # first step all zeros: unscaled
     kb[11, :, :] = 0.0
-    kb[11, 3, 127] = 5.0e4
+    kb[11, -1, -1] = 5.0e4
     s = gpu_scores(q, kb, a, "f16x2")
     s64 = ORC.scores_f64(q, kb, a)
     assert np.all(np.isfinite(s))
