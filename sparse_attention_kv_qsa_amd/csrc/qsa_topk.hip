@@ -144,10 +144,13 @@ __device__ __forceinline__ void hist_add(uint32_t *hsub, bool take, uint32_t bin
 
 // Radix select of the k largest (key, id) pairs among those `visit` yields
 // (key 0 = sentinel; n_sentinel of them among the visited).  k must be less
-// than the number of real keys.  ids are block ids < A.
+// than the number of real keys.  ids are block ids < A.  With `keys_only`,
+// a select that meets more keys equal to T than it still needs returns after
+// the key passes (by_id set, tied = the number of them to take, lowest ids
+// first) and leaves the id passes to the caller.
 template <class Visit>
 __device__ __forceinline__ Threshold radix_select(TopkShared &sh, Visit &&visit, uint32_t k, uint32_t n_sentinel,
-                                  int A) {
+                                  int A, bool keys_only = false) {
   const int wave = threadIdx.x >> 6;
   Threshold th;
   uint32_t kr = k;
@@ -169,6 +172,7 @@ __device__ __forceinline__ Threshold radix_select(TopkShared &sh, Visit &&visit,
   // More keys equal T = pref than are still needed: take the kr lowest ids.
   th.by_id = true;
   th.tied = kr;
+  if (keys_only) return th;
   const int idbits = 32 - __clz(uint32_t(A - 1));
   th.idtop = idbits >= 32 ? 0xFFFFFFFFu : ((1u << idbits) - 1u);
   for (int shift = 8 * ((idbits + 7) / 8 - 1); shift >= 0; shift -= 8) {
@@ -879,8 +883,58 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int A, 
         f(ok ? sh.cu.c.cid[i] : 0u, ok ? sh.cu.c.ckey[i] : 0u);
       }
     };
+    // Rows of up to 32 x 4096 blocks resolve a tie at the threshold with a
+    // bitmap of the tied ids in the sort's exchange words (free until the
+    // sort): one pass of atomic ORs and one prefix sum instead of up to three
+    // radix passes over the ids, and the tied winners leave in id order with
+    // no sorting; only the keys above the tie are ranked.
+    uint32_t *tbits = reinterpret_cast<uint32_t *>(sh.wbuf);
+    constexpr int kTieWordsPerThread = int(sizeof(sh.wbuf)) / 4 / NT;
+    const bool tie_bitmap = A <= 32 * kTieWordsPerThread * NT;  // workgroup-uniform
+    const int nbw = (A + 31) / 32;
+    if (tie_bitmap)  // cleared here; the select's barriers order it before use
+      for (int w = t; w < nbw; w += NT) tbits[w] = 0u;
     Threshold th;
-    if (uint32_t(k) < C) th = radix_select(sh, visit_cand, uint32_t(k), padC - C, A);
+    if (uint32_t(k) < C) th = radix_select(sh, visit_cand, uint32_t(k), padC - C, A, tie_bitmap);
+    if (th.by_id && tie_bitmap) {
+      const uint32_t T = th.pref;  // the whole threshold key
+      visit_cand([&](uint32_t id, uint32_t key) {
+        if (key == T && key != 0u) atomicOr(&tbits[id >> 5], 1u << (id & 31u));
+      });
+      compact<kLean>(visit_cand, [&](uint32_t, uint32_t key) { return key > T; }, &sh.nwin, sh.bkey,
+                     sh.bid, MAXK);
+      __syncthreads();
+      const int nabove = int(sh.nwin);  // = k - th.tied: they take ranks [0, nabove)
+      // Thread t owns bitmap words [W t, W t + W): ids in ascending order
+      // across the threads; the tied winners are the first th.tied set bits.
+      uint32_t wv[kTieWordsPerThread];
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int j = 0; j < kTieWordsPerThread; ++j) {
+        const int w = kTieWordsPerThread * t + j;
+        wv[j] = w < nbw ? tbits[w] : 0u;
+        cnt += uint32_t(__popc(wv[j]));
+      }
+      uint32_t total;
+      uint32_t p = block_excl_scan(cnt, sh.wsum, total);
+#pragma unroll
+      for (int j = 0; j < kTieWordsPerThread; ++j) {
+        uint32_t x = wv[j];
+        while (x != 0u && p < th.tied) {
+          const uint32_t b = uint32_t(__builtin_ctz(x));
+          x &= x - 1u;
+          orow[nabove + int(p)] = int(uint32_t(kTieWordsPerThread * t + j) * 32u + b);
+          ++p;
+        }
+      }
+      __syncthreads();  // the bitmap is read; the sort may reuse its words
+      // A row tied in bulk at its threshold is usually tied in bulk above it
+      // too, where the counting rank would refuse a bucket (about a
+      // microsecond lost): rank the keys above with the network directly.
+      if (nabove > 0)
+        sort_and_store(sh.bkey, sh.bid, nabove, nabove, nabove, orow, sh, sh.cu.xbuf, false);
+      return;
+    }
     compact<kLean>(visit_cand, [&](uint32_t id, uint32_t key) { return key != 0u && th.wins(id, key); },
             &sh.nwin, sh.bkey, sh.bid, MAXK);
     try_count = !th.by_id && th.tied <= kBucketCap;
