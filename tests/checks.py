@@ -1,7 +1,7 @@
 """Checkers shared by the oracle pins and the GPU parity tests.
 
 These do not compute selections themselves beyond tiny brute force; they
-judge a result against what the definition fixes:
+check a result against what the definition fixes:
 
 * ``score_gate``: max |s - s64| <= tol * max |s64| over the whole call (the
   FP64-relative gate; tol = 1e-6).
