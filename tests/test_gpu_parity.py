@@ -278,6 +278,19 @@ def test_topk_k_larger_than_row(a, k, path):
     assert np.all(ids[:, a:] == -1)
 
 
+@pytest.mark.parametrize("a,k", [(131072, 1024), (131073, 1024), (65538, 100), (4097, 2000)])
+def test_topk_tie_at_threshold(a, k):
+    """Rows whose k-th key is shared by many more elements than are still
+    needed (a tie at the threshold, resolved by id): rows of up to 131,072
+    blocks take the ids through a bitmap of the tied ids, longer ones through
+    radix passes over the id; both must give the lowest ids of the tie."""
+    rng = np.random.default_rng(a + k)
+    s = tie_rows(rng, 3, a, 40)
+    s[:, rng.choice(a, 37, replace=False)] = np.float32(50.0)  # a few distinct leaders
+    ids = check_topk(s, k, "per-row")
+    assert ids.shape[1] == k
+
+
 def clustered_rows(rng, a):
     """Rows whose best scores crowd into a few places: the whole-GPU path's
     groups holding more winners than they publish (re-read from the scores),
